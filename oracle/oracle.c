@@ -1,0 +1,287 @@
+/*
+ * CPU oracle for the DSpark drafter's proposal step.
+ *
+ * TEST INFRASTRUCTURE. This library exists only to check the GPU library.
+ * Only the test suite, the smoke entry point and the benchmark's CPU-baseline
+ * leg may load it. It shares no code, header or table with the GPU path and
+ * includes no HIP header.
+ *
+ * What it computes, one block b at a time, in the order the method states:
+ *
+ *  1. Projection: every prediction slot j of block b goes through the shared
+ *     lm_head, z_j[v] = sum_h x_j[h] * lm_head[v][h] (+ bias[v]). The drafter
+ *     owns no output head of its own and borrows the target's
+ *     (onnxruntime-genai PR #2490 "Export DSpark block drafters for Qwen 3.5
+ *     and 3.8", DSpark commit message; llama.cpp commit 6fed9f6 "spec: add
+ *     DSpark speculative decoding", first item). The bias is the -1e9 row
+ *     bias of an expanded reduced vocabulary (llama.cpp PR #26275 "dspark:
+ *     support speculators-format checkpoints", first commit message).
+ *  2. Markov chain: slot j is re-scored with the low-rank bigram bias of the
+ *     previous token, z'_j[v] = z_j[v] + sum_k markov_w2[v][k] *
+ *     markov_w1[prev_j][k]; prev_0 is the block's anchor and prev_j (j>0) is
+ *     the argmax of z'_{j-1} (llama.cpp commit 6fed9f6, item "spec: add DSpark
+ *     speculative decoding", the chained-bias formula).
+ *  3. Candidates: the top-k of the same biased scores per slot, for the tree /
+ *     lattice (lucebox PR #626 description: the tree's candidate top-k also
+ *     carries the Markov bias; onnxruntime-genai PR #2490, dspark_top_k).
+ *  4. Confidence: one scalar per prediction slot, sigma(sum_h x_j[h] *
+ *     conf_w[h]), read as the predicted survival probability; the block is cut
+ *     at the first slot below p_min (llama.cpp commit 6fed9f6, items "spec:
+ *     add confidence-based draft pruning for DSpark" and "dspark: fold
+ *     conf_min into p_min").
+ *
+ * Block layouts: anchor-first (every slot predicts; i_first_pred = 0) and the
+ * 1+N bonus-anchor layout (slot 0 holds the bonus token and is never read;
+ * i_first_pred = 1) (llama.cpp PR #26275, first commit message and
+ * "Format differences").
+ *
+ * Arithmetic: bf16 operands are decoded exactly, every sum is accumulated in
+ * double precision in increasing index order (a bf16*bf16 product is exact in
+ * double), and a value is rounded once to float only where the contract hands
+ * out a float: the biased scores z' on which argmax / top-k decide, and the
+ * confidence compared with p_min. fp32 hidden states are first rounded to
+ * bf16 (nearest, ties to even), since the contraction is bf16 x bf16.
+ * Argmax ties go to the lowest index; top-k orders by value descending, then
+ * index ascending.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_ERR (-1)
+
+/* Value of a bf16 bit pattern: a bf16 is the upper half of a binary32. */
+static double bf16_value(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* binary32 -> bf16, round to nearest, ties to even.
+ * Written as "pick the nearer of the two neighbouring bf16 values": lo is x
+ * truncated toward zero, hi the next bf16 of larger magnitude. */
+uint16_t oracle_bf16_round(float x)
+{
+    uint32_t u;
+    memcpy(&u, &x, sizeof u);
+    if (isnan(x))
+        return (uint16_t)((u >> 16) | 0x0040u);
+    if (isinf(x))
+        return (uint16_t)(u >> 16);
+    uint16_t lo = (uint16_t)(u >> 16);
+    uint16_t hi = (uint16_t)(lo + 1u);
+    double dx = (double)x;
+    double dlo = bf16_value(lo);
+    double dhi;
+    if ((hi & 0x7f80u) == 0x7f80u) /* the next magnitude is past the largest finite bf16 */
+        dhi = copysign(ldexp(1.0, 128), dx);
+    else
+        dhi = bf16_value(hi);
+    double elo = fabs(dx - dlo), ehi = fabs(dhi - dx);
+    if (elo < ehi)
+        return lo;
+    if (ehi < elo)
+        return hi;
+    return (lo & 1u) ? hi : lo;
+}
+
+double oracle_bf16_value(uint16_t bits) { return bf16_value(bits); }
+
+/* Row `row` of hidden [B*L, H] as exact doubles of its bf16 values. */
+static void load_hidden_row(const void* hidden, int hidden_is_f32, long row, int H, double* x)
+{
+    if (hidden_is_f32) {
+        const float* p = (const float*)hidden + row * (long)H;
+        for (int h = 0; h < H; ++h)
+            x[h] = bf16_value(oracle_bf16_round(p[h]));
+    } else {
+        const uint16_t* p = (const uint16_t*)hidden + row * (long)H;
+        for (int h = 0; h < H; ++h)
+            x[h] = bf16_value(p[h]);
+    }
+}
+
+/* Projection of the n_pred prediction rows of block b through lm_head.
+ * z[j*V + v] = sum_h x_j[h] * lm_head[v*H + h] (+ bias[v]), x_j = hidden row
+ * b*L + i_first_pred + j. */
+int oracle_block_logits(const void* hidden, int hidden_is_f32, const uint16_t* lm_head,
+                        const float* bias, int L, int H, int V, int i_first_pred, int b,
+                        double* z)
+{
+    int n_pred = L - i_first_pred;
+    if (n_pred <= 0 || H <= 0 || V <= 0 || b < 0)
+        return ORACLE_ERR;
+    double* x = (double*)malloc(sizeof(double) * (size_t)n_pred * (size_t)H);
+    if (!x)
+        return ORACLE_ERR;
+    for (int j = 0; j < n_pred; ++j)
+        load_hidden_row(hidden, hidden_is_f32, (long)b * L + i_first_pred + j, H, x + (size_t)j * H);
+
+#pragma omp parallel for schedule(static)
+    for (long v = 0; v < V; ++v) {
+        const uint16_t* w = lm_head + v * (long)H;
+        for (int j = 0; j < n_pred; ++j) {
+            const double* xj = x + (size_t)j * H;
+            double s = 0.0;
+            for (int h = 0; h < H; ++h)
+                s += xj[h] * bf16_value(w[h]);
+            if (bias)
+                s += (double)bias[v];
+            z[(size_t)j * V + v] = s;
+        }
+    }
+    free(x);
+    return ORACLE_OK;
+}
+
+/* Low-rank bigram bias of token `prev`: m[v] = sum_k w2[v][k] * w1[prev][k]. */
+int oracle_markov_bias(const uint16_t* w1, const uint16_t* w2, int V, int r, int prev, double* m)
+{
+    if (prev < 0 || prev >= V || r < 0)
+        return ORACLE_ERR;
+    if (r == 0) {
+        for (long v = 0; v < V; ++v)
+            m[v] = 0.0;
+        return ORACLE_OK;
+    }
+    const uint16_t* u = w1 + (long)prev * r;
+#pragma omp parallel for schedule(static)
+    for (long v = 0; v < V; ++v) {
+        const uint16_t* w = w2 + v * (long)r;
+        double s = 0.0;
+        for (int k = 0; k < r; ++k)
+            s += bf16_value(w[k]) * bf16_value(u[k]);
+        m[v] = s;
+    }
+    return ORACLE_OK;
+}
+
+/* Biased scores of one slot under a given previous token, rounded once to
+ * float: zp[v] = float(z_row[v] + m[v]). */
+int oracle_step_scores(const double* z_row, const uint16_t* w1, const uint16_t* w2, int V, int r,
+                       int prev, float* zp)
+{
+    double* m = (double*)malloc(sizeof(double) * (size_t)V);
+    if (!m)
+        return ORACLE_ERR;
+    int st = oracle_markov_bias(w1, w2, V, r, prev, m);
+    if (st == ORACLE_OK)
+        for (long v = 0; v < V; ++v)
+            zp[v] = (float)(z_row[v] + m[v]);
+    free(m);
+    return st;
+}
+
+/* Scalar argmax, first (lowest) index on ties. */
+int oracle_argmax(const float* zp, int V)
+{
+    int best = 0;
+    for (int v = 1; v < V; ++v)
+        if (zp[v] > zp[best])
+            best = v;
+    return best;
+}
+
+/* Top-k by k passes of the argmax scan, each skipping the ids already taken;
+ * yields value descending, index ascending among equal values. */
+int oracle_topk(const float* zp, int V, int k, int32_t* idx, float* val)
+{
+    if (k < 1 || k > V)
+        return ORACLE_ERR;
+    for (int t = 0; t < k; ++t) {
+        int best = -1;
+        for (int v = 0; v < V; ++v) {
+            int taken = 0;
+            for (int s = 0; s < t; ++s)
+                if (idx[s] == v)
+                    taken = 1;
+            if (taken)
+                continue;
+            if (best < 0 || zp[v] > zp[best])
+                best = v;
+        }
+        idx[t] = best;
+        val[t] = zp[best];
+    }
+    return ORACLE_OK;
+}
+
+/* The chain of one block over precomputed projections z [n_pred][V]. */
+int oracle_block_chain(const double* z, const uint16_t* w1, const uint16_t* w2, int V, int r,
+                       int anchor, int n_pred, int top_k, int32_t* tokens, int32_t* cand,
+                       float* cand_val)
+{
+    if (anchor < 0 || anchor >= V || n_pred <= 0 || top_k < 1 || top_k > V)
+        return ORACLE_ERR;
+    float* zp = (float*)malloc(sizeof(float) * (size_t)V);
+    if (!zp)
+        return ORACLE_ERR;
+    int prev = anchor;
+    int st = ORACLE_OK;
+    for (int j = 0; j < n_pred && st == ORACLE_OK; ++j) {
+        st = oracle_step_scores(z + (size_t)j * V, w1, w2, V, r, prev, zp);
+        if (st != ORACLE_OK)
+            break;
+        tokens[j] = oracle_argmax(zp, V);
+        st = oracle_topk(zp, V, top_k, cand + (size_t)j * top_k, cand_val + (size_t)j * top_k);
+        prev = tokens[j];
+    }
+    free(zp);
+    return st;
+}
+
+/* Confidence of one prediction slot: float(sigma(sum_h x[h] * conf_w[h])). */
+float oracle_conf(const void* hidden, int hidden_is_f32, const uint16_t* conf_w, int L, int H,
+                  int i_first_pred, int b, int j)
+{
+    double* x = (double*)malloc(sizeof(double) * (size_t)H);
+    if (!x)
+        return NAN;
+    load_hidden_row(hidden, hidden_is_f32, (long)b * L + i_first_pred + j, H, x);
+    double c = 0.0;
+    for (int h = 0; h < H; ++h)
+        c += x[h] * bf16_value(conf_w[h]);
+    free(x);
+    return (float)(1.0 / (1.0 + exp(-c)));
+}
+
+/* Prefix truncation: the first slot whose confidence is strictly below p_min,
+ * or n_pred when there is none. p_min = 0 therefore never truncates. */
+int oracle_truncate(const float* conf, int n_pred, float p_min)
+{
+    for (int j = 0; j < n_pred; ++j)
+        if (conf[j] < p_min)
+            return j;
+    return n_pred;
+}
+
+/* Everything for block b. z (may be NULL) receives the projections
+ * [n_pred][V]; with no conf_w, conf = 1 and length = n_pred. */
+int oracle_propose_block(const void* hidden, int hidden_is_f32, const uint16_t* lm_head,
+                         const float* bias, const uint16_t* w1, const uint16_t* w2,
+                         const uint16_t* conf_w, const int32_t* anchors, int L, int H, int V,
+                         int r, int i_first_pred, int top_k, float p_min, int b, double* z,
+                         int32_t* tokens, int32_t* cand, float* cand_val, float* conf,
+                         int32_t* length)
+{
+    int n_pred = L - i_first_pred;
+    double* zz = z ? z : (double*)malloc(sizeof(double) * (size_t)n_pred * (size_t)V);
+    if (!zz)
+        return ORACLE_ERR;
+    int st = oracle_block_logits(hidden, hidden_is_f32, lm_head, bias, L, H, V, i_first_pred, b, zz);
+    if (st == ORACLE_OK)
+        st = oracle_block_chain(zz, w1, w2, V, r, anchors[b], n_pred, top_k, tokens, cand, cand_val);
+    if (st == ORACLE_OK) {
+        for (int j = 0; j < n_pred; ++j)
+            conf[j] = conf_w ? oracle_conf(hidden, hidden_is_f32, conf_w, L, H, i_first_pred, b, j)
+                             : 1.0f;
+        *length = conf_w ? oracle_truncate(conf, n_pred, p_min) : n_pred;
+    }
+    if (!z)
+        free(zz);
+    return st;
+}

@@ -1,0 +1,66 @@
+"""Planted mistakes in the oracle must be caught by the pins.
+
+Each mutant is a copy of oracle.c with one plausible mistake (a dropped term,
+a wrong sign or index, a transposed operand, a wrong tie rule ...), compiled
+with gcc into a temporary directory. The pin suite must fail on every one of
+them; otherwise the pins would not be able to tell a correct oracle from a
+subtly wrong one.
+"""
+import os
+
+import pytest
+
+from oracle import SRC_PATH, Oracle, build, load
+from pins import ALL_PINS
+
+MUTANTS = {
+    "markov_dropped": ("zp[v] = (float)(z_row[v] + m[v]);", "zp[v] = (float)(z_row[v]);"),
+    "markov_sign": ("zp[v] = (float)(z_row[v] + m[v]);", "zp[v] = (float)(z_row[v] - m[v]);"),
+    "markov_w1_w2_swapped": ("const uint16_t* u = w1 + (long)prev * r;",
+                             "const uint16_t* u = w2 + (long)prev * r; w2 = w1;"),
+    "prev_never_updated": ("prev = tokens[j];", "prev = anchor;"),
+    "prev0_not_anchor": ("int prev = anchor;", "int prev = 0;"),
+    "argmax_last_tie": ("if (zp[v] > zp[best])\n            best = v;\n    return best;",
+                        "if (zp[v] >= zp[best])\n            best = v;\n    return best;"),
+    "bias_dropped": ("s += (double)bias[v];", "s += 0.0;"),
+    "bonus_slot_read": ("load_hidden_row(hidden, hidden_is_f32, (long)b * L + i_first_pred + j, H, x + (size_t)j * H);",
+                        "load_hidden_row(hidden, hidden_is_f32, (long)b * L + j, H, x + (size_t)j * H);"),
+    "lm_head_transposed": ("s += xj[h] * bf16_value(w[h]);",
+                           "s += xj[h] * bf16_value(lm_head[(long)h * V + v]);"),
+    "truncate_le": ("if (conf[j] < p_min)", "if (conf[j] <= p_min)"),
+    "sigmoid_sign": ("return (float)(1.0 / (1.0 + exp(-c)));", "return (float)(1.0 / (1.0 + exp(c)));"),
+    "rne_ties_down": ("return (lo & 1u) ? hi : lo;", "return lo;"),
+    "topk_no_exclusion": ("taken = 1;", "taken = 0;"),
+    "topk_last_tie": ("if (best < 0 || zp[v] > zp[best])", "if (best < 0 || zp[v] >= zp[best])"),
+    "conf_wrong_slot": ("load_hidden_row(hidden, hidden_is_f32, (long)b * L + i_first_pred + j, H, x);",
+                        "load_hidden_row(hidden, hidden_is_f32, (long)b * L + j, H, x);"),
+    "truncate_short": ("            return j;\n    return n_pred;", "            return j;\n    return n_pred - 1;"),
+    "markov_rank_short": ("for (int k = 0; k < r; ++k)", "for (int k = 1; k < r; ++k)"),
+    "hidden_f32_truncated": ("x[h] = bf16_value(oracle_bf16_round(p[h]));",
+                             "x[h] = bf16_value((uint16_t)(*(const uint32_t*)&p[h] >> 16));"),
+}
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(SRC_PATH) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, source, tmp_path):
+    old, new = MUTANTS[name]
+    assert source.count(old) == 1, f"mutation site for {name} not found exactly once"
+    src = tmp_path / "oracle_mutant.c"
+    src.write_text(source.replace(old, new))
+    lib = load(build(str(src), str(tmp_path / "liboracle_mutant.so")))
+    orc = Oracle(lib)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            caught.append(pin.__name__)
+        except ValueError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted mistake {name}"
