@@ -1,0 +1,158 @@
+#!/usr/bin/env python3
+"""Throughput of the DSpark proposal step on one MI355X.
+
+One step = one dspark_propose call over one batch of seeded synthetic input:
+lm_head projection, Markov chain over every slot, top-k candidates,
+confidence truncation. The default workload is the throughput case at the
+Qwen3.8-27B shape (B=64 blocks of L=16 anchor-first slots, H=5120,
+V=248320, r=128, top_k=4, p_min=0.3); inputs are resident in HBM before the
+timed region starts. Prints one JSON line.
+
+Per-kernel figures come from a second timed loop that issues the same two
+halves separately (dspark_logits, then dspark_chain) with HIP events on the
+launch stream between them.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+METRIC = "drafted tokens/s (B×L Markov-chain proposals) at Qwen3.8-27B shape; % roofline"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(inp, blocks: int) -> dict:
+    """The oracle as it stands, on the host cores, over the first `blocks` blocks."""
+    from oracle import Oracle
+    orc = Oracle()
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    orc.propose(inp, blocks=list(range(blocks)), keep_logits=False)
+    dt = time.perf_counter() - t0
+    toks = blocks * inp.cfg.n_pred
+    return {"value": toks / dt, "unit": "drafted tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{blocks} of {inp.cfg.B} blocks ({toks} drafted tokens) of the same "
+                      f"workload, {dt:.1f} s wall on {cores} OpenMP threads"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen38_27b_throughput")
+    ap.add_argument("--cpu-blocks", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the proposal step is built and measured on a "
+              "single MI355X; run it with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import dspark_block_drafter_amd as dsp
+    from devutil import to_device
+    from synthetic import CONFIGS, make_inputs
+
+    cfg = CONFIGS[args.workload]
+    t0 = time.perf_counter()
+    inp = make_inputs(cfg)
+    log(f"inputs for {cfg.name} generated in {time.perf_counter() - t0:.1f} s")
+    d = to_device(inp)
+    out = dsp.Outputs(cfg.B, cfg.L, cfg.V, cfg.top_k, cfg.layout, "cuda:0")
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def step():
+        dsp.propose(d["hidden"], d["lm_head"], d["markov_w1"], d["markov_w2"], d["anchors"],
+                    layout=cfg.layout, top_k=cfg.top_k, p_min=cfg.p_min,
+                    lm_head_bias=d["lm_head_bias"], conf_w=d["conf_w"], out=out, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done")
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step (events), {1e3 * wall / args.steps:.3f} ms/step (wall)")
+    assert dsp.read_flags(out) == 0
+
+    # Per-kernel split: the same kernels through dspark_logits + dspark_chain.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in evs:
+        e[0].record(stream)
+        dsp.logits(d["hidden"], d["lm_head"], layout=cfg.layout, lm_head_bias=d["lm_head_bias"],
+                   out=out.logits, stream=stream)
+        e[1].record(stream)
+        dsp.chain(out.logits, d["markov_w1"], d["markov_w2"], d["anchors"], B=cfg.B, L=cfg.L,
+                  layout=cfg.layout, top_k=cfg.top_k, p_min=cfg.p_min, hidden=d["hidden"],
+                  conf_w=d["conf_w"], out=out, stream=stream)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    gemm_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    chain_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    log(f"lm_head GEMM {gemm_ms * 1e3:.1f} us, chain+finalize {chain_ms * 1e3:.1f} us")
+
+    M, H, V, r, B, n = cfg.B * cfg.n_pred, cfg.H, cfg.V, cfg.r, cfg.B, cfg.n_pred
+    flops = 2.0 * M * H * V
+    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
+    # chain: per slot the B logits rows and markov_w2 are streamed, plus B rank-r gathers
+    chain_bytes = n * (B * V * 4 + V * r * 2 + B * r * 2)
+    chain_gbs = chain_bytes / (chain_ms * 1e-3) / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": cfg.drafted_tokens / (ms * 1e-3),
+        "unit": "drafted tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "L": cfg.L, "H": H, "V": V, "r": r,
+                   "top_k": cfg.top_k, "p_min": cfg.p_min, "layout": cfg.layout,
+                   "drafted_tokens_per_step": cfg.drafted_tokens},
+        "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": gemm_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": "lmhead_gemm", "us": gemm_ms * 1e3},
+        "roofline_chain": {"bound": "hbm", "achieved": chain_gbs, "peak": PEAK_HBM_GBS,
+                           "unit": "GB/s", "frac": chain_gbs / PEAK_HBM_GBS,
+                           "bytes": chain_bytes, "kernels": "chain_init + chain_step x n_pred + finalize",
+                           "us": chain_ms * 1e3},
+        "wall_ms_per_step": 1e3 * wall / args.steps,
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {args.cpu_blocks} blocks")
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_blocks)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

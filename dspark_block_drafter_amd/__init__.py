@@ -1,0 +1,247 @@
+"""DSpark drafter proposal step on MI355X (gfx950).
+
+Python binding of ``libdspark.so`` (C ABI declared in ``include/dspark.h``).
+This module only marshals arguments: it turns torch tensors into device
+pointers and the current HIP stream into a handle, and raises on a non-OK
+status. Every step of the computation runs in the library's HIP kernels;
+there is no Python or CPU fallback, and importing the binding fails loudly
+when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdspark.so")
+
+ANCHOR_FIRST = 0
+BONUS_ANCHOR = 1
+LAYOUTS = {"anchor_first": ANCHOR_FIRST, "bonus_anchor": BONUS_ANCHOR,
+           ANCHOR_FIRST: ANCHOR_FIRST, BONUS_ANCHOR: BONUS_ANCHOR}
+HIDDEN_BF16 = 0
+HIDDEN_F32 = 1
+
+OK = 0
+ERR_INVALID_ARG = -1
+ERR_UNSUPPORTED = -2
+ERR_WORKSPACE = -3
+ERR_HIP = -4
+
+FLAG_BAD_ANCHOR = 1
+FLAG_INTERNAL = 2
+
+MAX_TOP_K = 16
+MAX_RANK = 256
+
+EXPORTS = ("dspark_workspace_bytes", "dspark_propose", "dspark_logits", "dspark_chain",
+           "dspark_read_flags", "dspark_status_string")
+
+
+class DsparkError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+_LIB: Optional[ctypes.CDLL] = None
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+_sz = ctypes.c_size_t
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libdspark.so (built by ``__graft_entry__.build()``); never builds or falls back."""
+    global _LIB
+    if _LIB is not None and path == LIB_PATH:
+        return _LIB
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; "
+                          f"g.build()'` (hipcc, gfx950); there is no fallback path")
+    lib = ctypes.CDLL(path)
+    lib.dspark_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
+    lib.dspark_workspace_bytes.restype = _sz
+    lib.dspark_propose.argtypes = [_vp, _i, _vp, _vp, _vp, _vp, _vp, _vp,
+                                   _i, _i, _i, _i, _i, _i, _i, _f,
+                                   _vp, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp]
+    lib.dspark_propose.restype = _i
+    lib.dspark_logits.argtypes = [_vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]
+    lib.dspark_logits.restype = _i
+    lib.dspark_chain.argtypes = [_vp, _vp, _i, _vp, _vp, _vp, _vp,
+                                 _i, _i, _i, _i, _i, _i, _i, _f,
+                                 _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp]
+    lib.dspark_chain.restype = _i
+    lib.dspark_read_flags.argtypes = [_vp, ctypes.POINTER(ctypes.c_uint32), _vp]
+    lib.dspark_read_flags.restype = _i
+    lib.dspark_status_string.argtypes = [_i]
+    lib.dspark_status_string.restype = ctypes.c_char_p
+    if path == LIB_PATH:
+        _LIB = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().dspark_status_string(int(status)).decode()
+
+
+def workspace_bytes(B: int, L: int, V: int, top_k: int, layout="anchor_first") -> int:
+    return int(load_library().dspark_workspace_bytes(B, L, V, top_k, LAYOUTS[layout]))
+
+
+def n_pred_of(L: int, layout) -> int:
+    return L - (1 if LAYOUTS[layout] == BONUS_ANCHOR else 0)
+
+
+# ---------------------------------------------------------------------------
+# torch front-end (device memory and streams only)
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def _stream(t, stream) -> int:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check_dev(name, t, dtype, shape=None):
+    torch = _torch()
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    del torch
+
+
+def _hidden_dtype(hidden) -> int:
+    torch = _torch()
+    if hidden.dtype == torch.bfloat16:
+        return HIDDEN_BF16
+    if hidden.dtype == torch.float32:
+        return HIDDEN_F32
+    raise ValueError(f"hidden must be bfloat16 or float32, got {hidden.dtype}")
+
+
+class Outputs:
+    """Device buffers of one proposal (reusable across calls of the same shape)."""
+
+    def __init__(self, B: int, L: int, V: int, top_k: int, layout, device, *,
+                 with_cand_logits: bool = True, with_conf: bool = True):
+        torch = _torch()
+        n = n_pred_of(L, layout)
+        self.logits = torch.empty((B * n, V), dtype=torch.float32, device=device)
+        self.tokens = torch.empty((B, n), dtype=torch.int32, device=device)
+        self.candidates = torch.empty((B, n, top_k), dtype=torch.int32, device=device)
+        self.cand_logits = (torch.empty((B, n, top_k), dtype=torch.float32, device=device)
+                            if with_cand_logits else None)
+        self.conf = torch.empty((B, n), dtype=torch.float32, device=device) if with_conf else None
+        self.lengths = torch.empty((B,), dtype=torch.int32, device=device)
+        nbytes = workspace_bytes(B, L, V, top_k, layout)
+        self.workspace = torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=device)
+
+    def as_dict(self) -> dict:
+        return {"logits": self.logits, "tokens": self.tokens, "candidates": self.candidates,
+                "cand_logits": self.cand_logits, "conf": self.conf, "lengths": self.lengths}
+
+
+def propose(hidden, lm_head, markov_w1, markov_w2, anchors, *, layout="anchor_first", top_k=1,
+            p_min=0.0, lm_head_bias=None, conf_w=None, out: Optional[Outputs] = None,
+            stream=None) -> Outputs:
+    """Run dspark_propose on device tensors; returns the Outputs holding the results."""
+    torch = _torch()
+    lib = load_library()
+    B, L, H = hidden.shape
+    V = lm_head.shape[0]
+    r = 0 if markov_w1 is None else markov_w1.shape[1]
+    _check_dev("hidden", hidden, hidden.dtype)
+    _check_dev("lm_head", lm_head, torch.bfloat16, (V, H))
+    _check_dev("lm_head_bias", lm_head_bias, torch.float32, (V,))
+    _check_dev("markov_w1", markov_w1, torch.bfloat16, (V, r))
+    _check_dev("markov_w2", markov_w2, torch.bfloat16, (V, r))
+    _check_dev("conf_w", conf_w, torch.bfloat16, (H,))
+    _check_dev("anchors", anchors, torch.int32, (B,))
+    if out is None:
+        out = Outputs(B, L, V, top_k, layout, hidden.device)
+    st = lib.dspark_propose(
+        _ptr(hidden), _hidden_dtype(hidden), _ptr(lm_head), _ptr(lm_head_bias), _ptr(markov_w1),
+        _ptr(markov_w2), _ptr(conf_w), _ptr(anchors), B, L, H, V, r, LAYOUTS[layout], top_k,
+        float(p_min), _ptr(out.logits), _ptr(out.workspace), out.workspace.numel(),
+        _ptr(out.tokens), _ptr(out.candidates), _ptr(out.cand_logits), _ptr(out.conf),
+        _ptr(out.lengths), _stream(hidden, stream))
+    if st != OK:
+        raise DsparkError(st, "dspark_propose")
+    return out
+
+
+def logits(hidden, lm_head, *, layout="anchor_first", lm_head_bias=None, out=None, stream=None):
+    """Run dspark_logits (the lm_head projection alone); returns fp32 [B*n_pred, V]."""
+    torch = _torch()
+    lib = load_library()
+    B, L, H = hidden.shape
+    V = lm_head.shape[0]
+    _check_dev("hidden", hidden, hidden.dtype)
+    _check_dev("lm_head", lm_head, torch.bfloat16, (V, H))
+    _check_dev("lm_head_bias", lm_head_bias, torch.float32, (V,))
+    n = n_pred_of(L, layout)
+    if out is None:
+        out = torch.empty((B * n, V), dtype=torch.float32, device=hidden.device)
+    _check_dev("out", out, torch.float32, (B * n, V))
+    st = lib.dspark_logits(_ptr(hidden), _hidden_dtype(hidden), _ptr(lm_head), _ptr(lm_head_bias),
+                           B, L, H, V, LAYOUTS[layout], _ptr(out), _stream(hidden, stream))
+    if st != OK:
+        raise DsparkError(st, "dspark_logits")
+    return out
+
+
+def chain(logits_in, markov_w1, markov_w2, anchors, *, B, L, layout="anchor_first", top_k=1,
+          p_min=0.0, hidden=None, conf_w=None, out: Optional[Outputs] = None, stream=None) -> Outputs:
+    """Run dspark_chain on caller-provided projections ``logits_in`` [B*n_pred, V]."""
+    torch = _torch()
+    lib = load_library()
+    V = logits_in.shape[1]
+    r = 0 if markov_w1 is None else markov_w1.shape[1]
+    H = hidden.shape[2] if hidden is not None else (conf_w.shape[0] if conf_w is not None else 8)
+    n = n_pred_of(L, layout)
+    _check_dev("logits", logits_in, torch.float32, (B * n, V))
+    _check_dev("markov_w1", markov_w1, torch.bfloat16, (V, r))
+    _check_dev("markov_w2", markov_w2, torch.bfloat16, (V, r))
+    _check_dev("conf_w", conf_w, torch.bfloat16, (H,))
+    _check_dev("anchors", anchors, torch.int32, (B,))
+    if out is None:
+        out = Outputs(B, L, V, top_k, layout, logits_in.device)
+    hd = _hidden_dtype(hidden) if hidden is not None else HIDDEN_BF16
+    st = lib.dspark_chain(
+        _ptr(logits_in), _ptr(hidden), hd, _ptr(markov_w1), _ptr(markov_w2), _ptr(conf_w),
+        _ptr(anchors), B, L, H, V, r, LAYOUTS[layout], top_k, float(p_min), _ptr(out.workspace),
+        out.workspace.numel(), _ptr(out.tokens), _ptr(out.candidates), _ptr(out.cand_logits),
+        _ptr(out.conf), _ptr(out.lengths), _stream(logits_in, stream))
+    if st != OK:
+        raise DsparkError(st, "dspark_chain")
+    return out
+
+
+def read_flags(out: Outputs, stream=None) -> int:
+    """Flags word of the workspace after the stream drains (synchronises the stream)."""
+    lib = load_library()
+    flags = ctypes.c_uint32(0)
+    st = lib.dspark_read_flags(_ptr(out.workspace), ctypes.byref(flags),
+                               _stream(out.workspace, stream))
+    if st != OK:
+        raise DsparkError(st, "dspark_read_flags")
+    return int(flags.value)

@@ -1,0 +1,82 @@
+// Shared device helpers for the gfx950 kernels of libdspark.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dspark {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef unsigned long long u64;
+
+constexpr int kWave = 64;
+
+// 32x32x16 bf16 MFMA (CDNA4). Lane l supplies A[row = l % 32][k = 8 * (l / 32) + i]
+// and B[k = 8 * (l / 32) + i][col = l % 32], i = 0..7. The 16 accumulators of
+// lane l hold D[row = 8 * (g / 4) + 4 * (l / 32) + g % 4][col = l % 32], g = 0..15.
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Row of the 32x32 accumulator tile held in register g by lane l.
+__device__ __forceinline__ int acc_row(int g, int lane) {
+    return 8 * (g >> 2) + 4 * (lane >> 5) + (g & 3);
+}
+
+// fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return bf16_rne(lo) | (bf16_rne(hi) << 16);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Total order used for every argmax / top-k decision: larger score first,
+// then smaller id. A (score, id) pair maps to a 64-bit key whose unsigned
+// order is that order: the high word is the score's bits made monotone
+// (-0 is folded onto +0 first, so equal scores compare equal), the low word
+// is ~id.
+__device__ __forceinline__ uint32_t order_f32(float x) {
+    uint32_t u = __float_as_uint(x + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float unorder_f32(uint32_t k) {
+    uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+    return __uint_as_float(u);
+}
+__device__ __forceinline__ u64 make_key(float score, int id) {
+    return ((u64)order_f32(score) << 32) | (u64)(~(uint32_t)id);
+}
+__device__ __forceinline__ int key_id(u64 key) { return (int)(~(uint32_t)key); }
+__device__ __forceinline__ float key_score(u64 key) { return unorder_f32((uint32_t)(key >> 32)); }
+
+__device__ __forceinline__ u64 shfl_xor_u64(u64 v, int mask) {
+    uint32_t lo = __shfl_xor((uint32_t)v, mask, kWave);
+    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), mask, kWave);
+    return ((u64)hi << 32) | lo;
+}
+
+// Insert `key` into the descending list `list[0..K)`, keeping the K largest.
+template <int K>
+__device__ __forceinline__ void topk_insert(u64 (&list)[K], u64 key) {
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+        u64 hi = list[i] > key ? list[i] : key;
+        u64 lo = list[i] > key ? key : list[i];
+        list[i] = hi;
+        key = lo;
+    }
+}
+
+}  // namespace dspark

@@ -1,0 +1,231 @@
+// C ABI of libdspark: argument validation, workspace layout, launch sequence.
+//
+// Validation runs on the host before any HIP call; a rejected call enqueues
+// nothing. The block-uniformity requirement (every block has the same L
+// slots, B and L passed explicitly) follows llama.cpp commit 6fed9f6 "spec:
+// add DSpark speculative decoding", item "dflash: assert the markov head
+// block-uniformity invariant, require the conf head" (a broken layout fails
+// loudly instead of silently dropping the bias).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/dspark.h"
+#include "kernels.hpp"
+
+using namespace dspark;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr size_t kFlagsBytes = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+    size_t winners_off, partials_off, total;
+};
+
+// [flags (256 B)] [winners: n_pred*B u64] [partials: n_pred*B*nwg*top_k u64, top_k > 1]
+Layout workspace_layout(int B, int n_pred, int V, int top_k) {
+    Layout l;
+    l.winners_off = kFlagsBytes;
+    const size_t win = align_up((size_t)n_pred * (size_t)B * 8u);
+    l.partials_off = l.winners_off + win;
+    const size_t part =
+        top_k > 1 ? align_up((size_t)n_pred * B * (size_t)chain_workgroups(V) * top_k * 8u) : 0;
+    l.total = l.partials_off + part;
+    return l;
+}
+
+int first_pred(int layout) { return layout == DSPARK_LAYOUT_BONUS_ANCHOR ? 1 : 0; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks shared by every entry point that runs the chain.
+int check_sizes(int B, int L, int H, int V, int layout, int hidden_dtype) {
+    if (B <= 0 || L <= 0 || H <= 0 || V <= 0) return DSPARK_ERR_INVALID_ARG;
+    if (layout != DSPARK_LAYOUT_ANCHOR_FIRST && layout != DSPARK_LAYOUT_BONUS_ANCHOR)
+        return DSPARK_ERR_INVALID_ARG;
+    if (hidden_dtype != DSPARK_HIDDEN_BF16 && hidden_dtype != DSPARK_HIDDEN_F32)
+        return DSPARK_ERR_INVALID_ARG;
+    if (layout == DSPARK_LAYOUT_BONUS_ANCHOR && L < 2) return DSPARK_ERR_INVALID_ARG;
+    // every index computed on the device must fit in 32 bits where it is one
+    const long n_pred = L - first_pred(layout);
+    if ((long)B * L > 0x7fffffffL / 2 || (long)B * n_pred * (long)V > (1L << 53))
+        return DSPARK_ERR_UNSUPPORTED;
+    if (V >= 0x7fffffff - 1024 || H % 8 != 0) return DSPARK_ERR_UNSUPPORTED;
+    return DSPARK_OK;
+}
+
+int check_chain_args(int V, int r, int top_k, float p_min, const void* w1, const void* w2) {
+    if (top_k < 1 || top_k > DSPARK_MAX_TOP_K || top_k > V) return DSPARK_ERR_INVALID_ARG;
+    if (r < 0) return DSPARK_ERR_INVALID_ARG;
+    if (r > 0 && (!w1 || !w2)) return DSPARK_ERR_INVALID_ARG;
+    if (r == 0 && (w1 || w2)) return DSPARK_ERR_INVALID_ARG;
+    if (isnan(p_min)) return DSPARK_ERR_INVALID_ARG;
+    if (r % 8 != 0 || r > DSPARK_MAX_RANK) return DSPARK_ERR_UNSUPPORTED;
+    if (!aligned16(w1) || !aligned16(w2)) return DSPARK_ERR_UNSUPPORTED;
+    return DSPARK_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP; }
+
+int run_chain(const float* logits, const void* hidden, int hidden_dtype, const uint16_t* w1,
+              const uint16_t* w2, const uint16_t* conf_w, const int32_t* anchors, int B, int L,
+              int H, int V, int r, int layout, int top_k, float p_min, void* workspace,
+              int32_t* tokens, int32_t* candidates, float* cand_logits, float* conf,
+              int32_t* lengths, hipStream_t stream) {
+    const int i_first = first_pred(layout);
+    const int n_pred = L - i_first;
+    const Layout wl = workspace_layout(B, n_pred, V, top_k);
+    char* ws = static_cast<char*>(workspace);
+
+    ChainArgs c;
+    c.logits = logits;
+    c.w1 = w1;
+    c.w2 = w2;
+    c.anchors = anchors;
+    c.winners = reinterpret_cast<unsigned long long*>(ws + wl.winners_off);
+    c.partials = top_k > 1 ? reinterpret_cast<unsigned long long*>(ws + wl.partials_off) : nullptr;
+    c.flags = reinterpret_cast<uint32_t*>(ws);
+    c.B = B;
+    c.V = V;
+    c.r = r;
+    c.n_pred = n_pred;
+    c.top_k = top_k;
+    c.nwg = chain_workgroups(V);
+
+    hipError_t e = launch_chain_init(c, stream);
+    for (int j = 0; j < n_pred && e == hipSuccess; ++j) e = launch_chain_step(c, j, stream);
+    if (e != hipSuccess) return DSPARK_ERR_HIP;
+
+    FinalArgs f;
+    f.winners = c.winners;
+    f.partials = c.partials;
+    f.hidden = hidden;
+    f.conf_w = conf_w;
+    f.tokens = tokens;
+    f.candidates = candidates;
+    f.cand_logits = cand_logits;
+    f.conf = conf;
+    f.lengths = lengths;
+    f.flags = c.flags;
+    f.B = B;
+    f.L = L;
+    f.H = H;
+    f.n_pred = n_pred;
+    f.i_first = i_first;
+    f.top_k = top_k;
+    f.nwg = c.nwg;
+    f.hidden_f32 = hidden_dtype == DSPARK_HIDDEN_F32;
+    f.p_min = p_min;
+    return hip_status(launch_finalize(f, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dspark_workspace_bytes(int B, int L, int V, int top_k, int layout) {
+    if (B <= 0 || V <= 0 || top_k < 1 || top_k > DSPARK_MAX_TOP_K) return 0;
+    if (layout != DSPARK_LAYOUT_ANCHOR_FIRST && layout != DSPARK_LAYOUT_BONUS_ANCHOR) return 0;
+    const int n_pred = L - first_pred(layout);
+    if (n_pred <= 0) return 0;
+    return workspace_layout(B, n_pred, V, top_k).total;
+}
+
+int dspark_logits(const void* hidden, int hidden_dtype, const uint16_t* lm_head,
+                  const float* lm_head_bias, int B, int L, int H, int V, int layout, float* logits,
+                  void* stream) {
+    int st = check_sizes(B, L, H, V, layout, hidden_dtype);
+    if (st != DSPARK_OK) return st;
+    if (!hidden || !lm_head || !logits) return DSPARK_ERR_INVALID_ARG;
+    if (!aligned16(hidden) || !aligned16(lm_head)) return DSPARK_ERR_UNSUPPORTED;
+    const int i_first = first_pred(layout);
+    GemmArgs g;
+    g.hidden = hidden;
+    g.lm_head = lm_head;
+    g.bias = lm_head_bias;
+    g.out = logits;
+    g.n_pred = L - i_first;
+    g.M = B * g.n_pred;
+    g.N = V;
+    g.K = H;
+    g.L = L;
+    g.i_first = i_first;
+    return hip_status(launch_lmhead_gemm(g, hidden_dtype == DSPARK_HIDDEN_F32,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int dspark_chain(const float* logits, const void* hidden, int hidden_dtype,
+                 const uint16_t* markov_w1, const uint16_t* markov_w2, const uint16_t* conf_w,
+                 const int32_t* anchors, int B, int L, int H, int V, int r, int layout, int top_k,
+                 float p_min, void* workspace, size_t workspace_bytes, int32_t* tokens,
+                 int32_t* candidates, float* cand_logits, float* conf, int32_t* lengths,
+                 void* stream) {
+    int st = check_sizes(B, L, H, V, layout, hidden_dtype);
+    if (st != DSPARK_OK) return st;
+    st = check_chain_args(V, r, top_k, p_min, markov_w1, markov_w2);
+    if (st != DSPARK_OK) return st;
+    if (!logits || !anchors || !tokens || !candidates || !lengths) return DSPARK_ERR_INVALID_ARG;
+    if (conf_w && !hidden) return DSPARK_ERR_INVALID_ARG;
+    if (conf_w && (!aligned16(conf_w) || !aligned16(hidden))) return DSPARK_ERR_UNSUPPORTED;
+    if (!workspace) return DSPARK_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return DSPARK_ERR_WORKSPACE;
+    if (workspace_bytes < dspark_workspace_bytes(B, L, V, top_k, layout)) return DSPARK_ERR_WORKSPACE;
+    if (!aligned16(logits)) return DSPARK_ERR_UNSUPPORTED;
+    return run_chain(logits, hidden, hidden_dtype, markov_w1, markov_w2, conf_w, anchors, B, L, H,
+                     V, r, layout, top_k, p_min, workspace, tokens, candidates, cand_logits, conf,
+                     lengths, static_cast<hipStream_t>(stream));
+}
+
+int dspark_propose(const void* hidden, int hidden_dtype, const uint16_t* lm_head,
+                   const float* lm_head_bias, const uint16_t* markov_w1,
+                   const uint16_t* markov_w2, const uint16_t* conf_w, const int32_t* anchors,
+                   int B, int L, int H, int V, int r, int layout, int top_k, float p_min,
+                   float* logits, void* workspace, size_t workspace_bytes, int32_t* tokens,
+                   int32_t* candidates, float* cand_logits, float* conf, int32_t* lengths,
+                   void* stream) {
+    int st = check_sizes(B, L, H, V, layout, hidden_dtype);
+    if (st != DSPARK_OK) return st;
+    st = check_chain_args(V, r, top_k, p_min, markov_w1, markov_w2);
+    if (st != DSPARK_OK) return st;
+    if (!hidden || !lm_head || !logits || !anchors || !tokens || !candidates || !lengths)
+        return DSPARK_ERR_INVALID_ARG;
+    if (!aligned16(hidden) || !aligned16(lm_head) || !aligned16(logits) ||
+        (conf_w && !aligned16(conf_w)))
+        return DSPARK_ERR_UNSUPPORTED;
+    if (!workspace) return DSPARK_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return DSPARK_ERR_WORKSPACE;
+    if (workspace_bytes < dspark_workspace_bytes(B, L, V, top_k, layout)) return DSPARK_ERR_WORKSPACE;
+
+    st = dspark_logits(hidden, hidden_dtype, lm_head, lm_head_bias, B, L, H, V, layout, logits,
+                       stream);
+    if (st != DSPARK_OK) return st;
+    return run_chain(logits, hidden, hidden_dtype, markov_w1, markov_w2, conf_w, anchors, B, L, H,
+                     V, r, layout, top_k, p_min, workspace, tokens, candidates, cand_logits, conf,
+                     lengths, static_cast<hipStream_t>(stream));
+}
+
+int dspark_read_flags(const void* workspace, uint32_t* flags, void* stream) {
+    if (!workspace || !flags) return DSPARK_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(flags, workspace, sizeof(uint32_t), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return DSPARK_ERR_HIP;
+    return hip_status(hipStreamSynchronize(s));
+}
+
+const char* dspark_status_string(int status) {
+    switch (status) {
+        case DSPARK_OK: return "ok";
+        case DSPARK_ERR_INVALID_ARG: return "invalid argument";
+        case DSPARK_ERR_UNSUPPORTED: return "unsupported size or alignment";
+        case DSPARK_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case DSPARK_ERR_HIP: return "HIP runtime error while enqueuing";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// Host-side launchers of the gfx950 kernels (internal to libdspark).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dspark {
+
+// ---- lm_head projection ---------------------------------------------------
+struct GemmArgs {
+    const void* hidden;      // [B, L, H] bf16 bits or fp32
+    const uint16_t* lm_head; // [V, H] bf16 bits
+    const float* bias;       // [V] or nullptr
+    float* out;              // [M, V], M = B * n_pred
+    int M, N, K;             // M rows, N = V, K = H
+    int L, n_pred, i_first;  // row m reads hidden row (m / n_pred) * L + i_first + m % n_pred
+};
+hipError_t launch_lmhead_gemm(const GemmArgs& a, bool hidden_f32, hipStream_t stream);
+
+// ---- Markov chain -----------------------------------------------------------
+// Columns of the vocabulary handled by one workgroup of a chain step.
+constexpr int kChainTileV = 512;
+inline int chain_workgroups(int V) { return (V + kChainTileV - 1) / kChainTileV; }
+
+struct ChainArgs {
+    const float* logits;       // [B * n_pred, V]
+    const uint16_t* w1;        // [V, r] bf16 bits (nullptr iff r == 0)
+    const uint16_t* w2;        // [V, r] bf16 bits
+    const int32_t* anchors;    // [B]
+    unsigned long long* winners;   // [n_pred, B] running argmax keys
+    unsigned long long* partials;  // [n_pred, B, nwg, top_k] per-workgroup top-k keys (top_k > 1)
+    uint32_t* flags;
+    int B, V, r, n_pred, top_k, nwg;
+};
+hipError_t launch_chain_init(const ChainArgs& a, hipStream_t stream);
+hipError_t launch_chain_step(const ChainArgs& a, int j, hipStream_t stream);
+
+struct FinalArgs {
+    const unsigned long long* winners;
+    const unsigned long long* partials;
+    const void* hidden;        // [B, L, H] (confidence head only)
+    const uint16_t* conf_w;    // [H] or nullptr
+    int32_t* tokens;           // [B, n_pred]
+    int32_t* candidates;       // [B, n_pred, top_k]
+    float* cand_logits;        // [B, n_pred, top_k] or nullptr
+    float* conf;               // [B, n_pred] or nullptr
+    int32_t* lengths;          // [B]
+    uint32_t* flags;
+    int B, L, H, n_pred, i_first, top_k, nwg;
+    int hidden_f32;
+    float p_min;
+};
+hipError_t launch_finalize(const FinalArgs& a, hipStream_t stream);
+
+}  // namespace dspark

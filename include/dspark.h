@@ -1,0 +1,185 @@
+/*
+ * dspark.h -- C ABI of libdspark, the DSpark drafter's proposal step on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The proposal step turns the drafter's hidden states for B blocks of L
+ * slots into draft tokens:
+ *
+ *   1. lm_head projection. Each prediction slot's hidden state goes through
+ *      the vocabulary head that the drafter shares with its target model:
+ *      logits[b*n_pred + j][v] = sum_h hidden[b][i_first_pred + j][h] *
+ *      lm_head[v][h] (+ lm_head_bias[v]).
+ *      Sources: onnxruntime-genai PR #2490 "Export DSpark block drafters for
+ *      Qwen 3.5 and 3.8" (DSpark commit message: no head of its own, the
+ *      target's is shared); llama.cpp PR #26275 "dspark: support
+ *      speculators-format checkpoints" (first commit message: the -1e9 bias on
+ *      rows a reduced draft vocabulary cannot produce).
+ *   2. Markov chain. Slot j's scores get the low-rank bigram bias of the
+ *      previous token: z'_j[v] = logits_j[v] + sum_k markov_w2[v][k] *
+ *      markov_w1[prev_j][k], with prev_0 = the block's anchor and prev_j =
+ *      argmax_v z'_{j-1}[v]; all blocks advance together, one slot at a time.
+ *      Source: llama.cpp commit 6fed9f6 "spec: add DSpark speculative
+ *      decoding", item of the same name (the chained-bias formula,
+ *      vectorised across blocks).
+ *   3. Candidates. The top_k ids of z'_j per slot form the candidate lattice
+ *      for tree / lattice verification; the Markov bias applies to them too.
+ *      Sources: lucebox PR #626 "feat(qwen38): add adaptive concurrent DSpark
+ *      speculation" (description); onnxruntime-genai PR #2490 (dspark_top_k).
+ *   4. Confidence truncation. conf[b][j] = sigmoid(sum_h hidden[b][i_first_pred
+ *      + j][h] * conf_w[h]) is the predicted survival probability of the
+ *      slot; lengths[b] is the first slot j with conf < p_min (n_pred if none;
+ *      p_min = 0 disables the cut).
+ *      Source: llama.cpp commit 6fed9f6, items "spec: add confidence-based
+ *      draft pruning for DSpark" and "dspark: fold conf_min into p_min".
+ *
+ * Block layout (llama.cpp PR #26275, first commit message and "Format
+ * differences"): DSPARK_LAYOUT_ANCHOR_FIRST -- every slot predicts
+ * (sample_from_anchor = true, i_first_pred = 0, n_pred = L);
+ * DSPARK_LAYOUT_BONUS_ANCHOR -- the 1+N fill-in block whose slot 0 carries
+ * the bonus token and is never read (sample_from_anchor = false,
+ * i_first_pred = 1, n_pred = L - 1).
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked DEVICE are device (HBM) pointers; every array is dense
+ *    and row-major. bf16 arrays are passed as their uint16_t bit patterns.
+ *  - The caller owns every buffer. The library allocates and frees nothing
+ *    and keeps no global mutable state; calls that use distinct workspaces
+ *    and outputs may run concurrently.
+ *  - `stream` is a hipStream_t (NULL = the default stream). All device work
+ *    is enqueued asynchronously on it; outputs are valid once the stream
+ *    reaches that point. The host never synchronises inside these calls.
+ *  - Arguments are validated on the host before anything is enqueued; on a
+ *    validation failure nothing is enqueued and the status says why.
+ *  - Numerics: hidden and weights are bf16 (fp32 hidden is rounded to bf16,
+ *    nearest-even, as it is staged); every product is accumulated in fp32.
+ *    Argmax ties go to the lowest id; candidates are ordered by score
+ *    descending, then id ascending. Results are bit-for-bit deterministic
+ *    for a given input.
+ *  - Anchors and previous tokens must lie in [0, V). The kernels never read
+ *    out of bounds: an out-of-range anchor is replaced by 0 and raises
+ *    DSPARK_FLAG_BAD_ANCHOR in the workspace flags (see dspark_read_flags).
+ *    Inputs must be finite; results for NaN / Inf inputs are undefined,
+ *    except in the bonus slot, which is never read.
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DSPARK_OK = 0,
+    DSPARK_ERR_INVALID_ARG = -1, /* a size, pointer, enum or p_min is not acceptable      */
+    DSPARK_ERR_UNSUPPORTED = -2, /* valid, but outside what the kernels implement          */
+    DSPARK_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than dspark_workspace_bytes */
+    DSPARK_ERR_HIP = -4          /* the HIP runtime reported an error while enqueuing     */
+} dspark_status;
+
+typedef enum {
+    DSPARK_LAYOUT_ANCHOR_FIRST = 0,
+    DSPARK_LAYOUT_BONUS_ANCHOR = 1
+} dspark_layout;
+
+typedef enum {
+    DSPARK_HIDDEN_BF16 = 0,
+    DSPARK_HIDDEN_F32 = 1
+} dspark_dtype;
+
+/* Device-side flags accumulated in the workspace by a call. */
+#define DSPARK_FLAG_BAD_ANCHOR 1u   /* an anchor was outside [0, V)                      */
+#define DSPARK_FLAG_INTERNAL 2u     /* the candidate merge disagreed with the chain's argmax */
+
+/* Limits checked by every entry point. */
+#define DSPARK_MAX_TOP_K 16
+#define DSPARK_MAX_RANK 256
+
+/*
+ * Bytes of device workspace that dspark_propose / dspark_chain need for these
+ * sizes (pure host function, no HIP call). Returns 0 if the sizes are invalid.
+ * The workspace holds the per-slot running argmax words, the per-workgroup
+ * top-k partial lists (top_k > 1 only) and the flags word. Its contents need
+ * no initialisation and are overwritten by every call.
+ */
+size_t dspark_workspace_bytes(int B, int L, int V, int top_k, int layout);
+
+/*
+ * The whole proposal step: projection, Markov chain, candidates, confidence
+ * truncation.
+ *
+ *   hidden        DEVICE [B, L, H], bf16 (hidden_dtype = DSPARK_HIDDEN_BF16)
+ *                 or fp32 (DSPARK_HIDDEN_F32). Under the bonus-anchor layout
+ *                 slot 0 of every block is not read.
+ *   lm_head       DEVICE bf16 [V, H] (one row per vocabulary id).
+ *   lm_head_bias  DEVICE fp32 [V], or NULL for no bias.
+ *   markov_w1     DEVICE bf16 [V, r]; the row of the previous token is used.
+ *   markov_w2     DEVICE bf16 [V, r]; maps the rank-r code to the vocabulary.
+ *                 Both NULL iff r == 0 (no Markov head: plain argmax).
+ *   conf_w        DEVICE bf16 [H], or NULL: no confidence head, conf = 1 and
+ *                 lengths = n_pred.
+ *   anchors       DEVICE int32 [B], each in [0, V).
+ *   B, L, H, V, r sizes; H and r multiples of 8, r <= DSPARK_MAX_RANK.
+ *   layout        dspark_layout.
+ *   top_k         candidates per slot, 1 <= top_k <= min(V, DSPARK_MAX_TOP_K).
+ *   p_min         truncation threshold (not NaN); 0 never truncates.
+ *   logits        DEVICE fp32 [B*n_pred, V] output: the projection (row
+ *                 b*n_pred + j), bias included, Markov term excluded.
+ *   workspace     DEVICE scratch of at least dspark_workspace_bytes(...)
+ *                 bytes, 256-byte aligned.
+ *   tokens        DEVICE int32 [B, n_pred] output: the greedy chain.
+ *   candidates    DEVICE int32 [B, n_pred, top_k] output; candidates[..., 0]
+ *                 equals tokens.
+ *   cand_logits   DEVICE fp32 [B, n_pred, top_k] output (z' of each
+ *                 candidate), or NULL.
+ *   conf          DEVICE fp32 [B, n_pred] output, or NULL.
+ *   lengths       DEVICE int32 [B] output. All n_pred slots are always
+ *                 drafted; lengths marks how many survive the cut.
+ * Returns a dspark_status.
+ */
+int dspark_propose(const void* hidden, int hidden_dtype, const uint16_t* lm_head,
+                   const float* lm_head_bias, const uint16_t* markov_w1,
+                   const uint16_t* markov_w2, const uint16_t* conf_w, const int32_t* anchors,
+                   int B, int L, int H, int V, int r, int layout, int top_k, float p_min,
+                   float* logits, void* workspace, size_t workspace_bytes, int32_t* tokens,
+                   int32_t* candidates, float* cand_logits, float* conf, int32_t* lengths,
+                   void* stream);
+
+/*
+ * Step 1 alone: the lm_head projection into `logits` (same arguments and
+ * layout as in dspark_propose). Needs no workspace.
+ */
+int dspark_logits(const void* hidden, int hidden_dtype, const uint16_t* lm_head,
+                  const float* lm_head_bias, int B, int L, int H, int V, int layout,
+                  float* logits, void* stream);
+
+/*
+ * Steps 2-4 on projections the caller provides: `logits` is an INPUT here
+ * (DEVICE fp32 [B*n_pred, V], laid out as dspark_propose writes it), and
+ * `hidden` is read only by the confidence head (may be NULL when conf_w is
+ * NULL). Every other argument is as in dspark_propose.
+ */
+int dspark_chain(const float* logits, const void* hidden, int hidden_dtype,
+                 const uint16_t* markov_w1, const uint16_t* markov_w2, const uint16_t* conf_w,
+                 const int32_t* anchors, int B, int L, int H, int V, int r, int layout,
+                 int top_k, float p_min, void* workspace, size_t workspace_bytes,
+                 int32_t* tokens, int32_t* candidates, float* cand_logits, float* conf,
+                 int32_t* lengths, void* stream);
+
+/*
+ * Copies the flags word of `workspace` (written by the last dspark_propose /
+ * dspark_chain on it) to *flags after `stream` has drained; this call does
+ * synchronise the stream. Returns a dspark_status.
+ */
+int dspark_read_flags(const void* workspace, uint32_t* flags, void* stream);
+
+/* Static, human-readable text for a status code. */
+const char* dspark_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H */

@@ -1,0 +1,187 @@
+"""GPU parity: the HIP path (called through the C ABI) against the CPU oracle.
+
+Small cases run the oracle on every block; they span several GEMM and chain
+tiles, ragged M / N / K tails, both block layouts, fp32 and bf16 hidden
+states, ranks from 0 to 256, top_k from 1 to 16 and more than 64 blocks. The
+full-size workloads are checked on sampled blocks (every block's chain is
+independent, so a sampled block is checked completely: all its logits, every
+slot's token and candidates, its confidences and its cut).
+"""
+from __future__ import annotations
+
+import sys
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+from oracle.check import check
+from synthetic import CONFIGS, make_inputs, make_small
+from synthetic.inputs import BONUS_ANCHOR
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import dspark_block_drafter_amd as dsp
+    dsp.load_library()
+    return torch.device("cuda:0")
+
+
+def _gpu(inp):
+    from devutil import run_propose, to_host
+    return to_host(run_propose(inp))
+
+
+SMALL = {
+    "tiny": lambda: make_inputs(CONFIGS["tiny"]),
+    "ragged_conf": lambda: make_small(3, 5, 264, 1000, 24, top_k=3, conf=True, p_min=0.45, seed=1),
+    "bonus_f32_v777": lambda: make_small(5, 7, 136, 777, 16, top_k=4, layout=BONUS_ANCHOR,
+                                         hidden_f32=True, conf=True, p_min=0.5, conf_trend=True,
+                                         seed=2),
+    "B70_two_groups": lambda: make_small(70, 3, 64, 2100, 8, top_k=2, seed=3, w_std=0.3),
+    "B40_k16_r128": lambda: make_small(40, 4, 520, 5000, 128, top_k=16, conf=True, p_min=0.3,
+                                       seed=4),
+    "r0_plain_argmax": lambda: make_small(4, 6, 96, 3000, 0, top_k=5, seed=5),
+    "topk_equals_V": lambda: make_small(2, 3, 16, 8, 8, top_k=8, seed=6),
+    "single_slot": lambda: make_small(1, 1, 32, 33, 8, top_k=1, seed=7),
+    "mid_gemm_M33": lambda: make_small(11, 3, 1032, 4097, 32, top_k=2, seed=8),
+    "rank256": lambda: make_small(6, 4, 128, 1536, 256, top_k=3, seed=9, w_std=0.2),
+    "reduced_vocab": lambda: make_small(4, 7, 176, 4096, 64, top_k=4, layout=BONUS_ANCHOR,
+                                        reachable=300, conf=True, p_min=0.5, conf_trend=True,
+                                        seed=10),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_parity(dev, orc, name):
+    inp = SMALL[name]()
+    _say(f"[parity] {name}: {inp.cfg}")
+    g = _gpu(inp)
+    reps = check(orc, inp, g)
+    ties = sum(r["near_tie"] for r in reps)
+    err = max(r["max_logit_err"] for r in reps)
+    _say(f"[parity] {name}: ok, max logit err {err:.3g}, near ties {ties}")
+    if inp.reachable is not None:
+        allowed = set(int(x) for x in inp.reachable)
+        assert set(g["tokens"].ravel().tolist()) <= allowed
+        assert set(g["candidates"].ravel().tolist()) <= allowed
+
+
+def test_chain_alone_on_oracle_logits(dev, orc):
+    """The chain kernel fed the oracle's own projections (rounded to fp32 on the
+    host), so chain errors cannot hide behind GEMM errors."""
+    import torch
+
+    import dspark_block_drafter_amd as dsp
+    from devutil import to_device
+    inp = make_small(9, 6, 64, 3333, 64, top_k=4, conf=True, p_min=0.4, seed=11, w_std=0.3)
+    z = np.concatenate([orc.block_logits(inp, b) for b in range(inp.cfg.B)]).astype(np.float32)
+    d = to_device(inp)
+    zt = torch.from_numpy(z).to(dev)
+    res = dsp.chain(zt, d["markov_w1"], d["markov_w2"], d["anchors"], B=inp.cfg.B, L=inp.cfg.L,
+                    layout=inp.cfg.layout, top_k=4, p_min=inp.cfg.p_min, hidden=d["hidden"],
+                    conf_w=d["conf_w"])
+    torch.cuda.synchronize()
+    g = {k: (None if v is None else v.cpu().numpy()) for k, v in res.as_dict().items()}
+    g["logits"] = None
+    check(orc, inp, g)
+    assert dsp.read_flags(res) == 0
+
+
+def test_logits_alone(dev, orc):
+    import torch
+
+    import dspark_block_drafter_amd as dsp
+    from devutil import to_device
+    inp = make_small(7, 5, 328, 2500, 8, seed=12, layout=BONUS_ANCHOR)
+    inp = replace(inp, lm_head_bias=np.linspace(-2, 2, 2500).astype(np.float32))
+    d = to_device(inp)
+    out = dsp.logits(d["hidden"], d["lm_head"], layout=BONUS_ANCHOR, lm_head_bias=d["lm_head_bias"])
+    torch.cuda.synchronize()
+    g = out.cpu().numpy().astype(np.float64)
+    for b in range(inp.cfg.B):
+        z = orc.block_logits(inp, b)
+        np.testing.assert_allclose(g[b * 4:(b + 1) * 4], z, atol=2e-2, rtol=0)
+
+
+def test_bonus_slot_never_read(dev):
+    inp = make_small(3, 7, 64, 1024, 16, top_k=3, layout=BONUS_ANCHOR, conf=True, p_min=0.5, seed=13)
+    h = inp.hidden.copy()
+    h[:, 0, :] = 0x7FC0  # NaN in every bonus slot
+    a, b = _gpu(inp), _gpu(replace(inp, hidden=h))
+    for k in ("logits", "tokens", "candidates", "cand_logits", "conf", "lengths"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_deterministic(dev):
+    inp = make_small(33, 5, 256, 7000, 64, top_k=4, conf=True, p_min=0.3, seed=14)
+    a, b = _gpu(inp), _gpu(inp)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_bad_anchor_raises_flag_without_fault(dev):
+    import dspark_block_drafter_amd as dsp
+    from devutil import run_propose
+    inp = make_small(2, 3, 32, 200, 8, top_k=2, seed=15)
+    bad = replace(inp, anchors=np.array([5, 200 + 17], np.int32))
+    res = run_propose(bad)
+    assert dsp.read_flags(res) & dsp.FLAG_BAD_ANCHOR
+    res = run_propose(inp)
+    assert dsp.read_flags(res) == 0
+
+
+def test_workspace_reuse_across_shapes(dev, orc):
+    """One Outputs/workspace reused by a second, smaller call of the same shape
+    family: stale contents from the first call must not leak."""
+    import dspark_block_drafter_amd as dsp
+    from devutil import run_propose, to_host
+    big = make_small(8, 4, 64, 2048, 16, top_k=4, seed=16)
+    run_propose(big)
+    small = make_small(8, 4, 64, 2048, 16, top_k=4, seed=17)
+    out = dsp.Outputs(8, 4, 2048, 4, "anchor_first", "cuda:0")
+    run_propose(big, out=out)
+    g = to_host(run_propose(small, out=out))
+    check(orc, small, g)
+
+
+# ---- full-size workloads, sampled blocks ------------------------------------
+
+FULL = {
+    "qwen3_8b": [0],
+    "gemma4_26b_a4b": [0, 1, 2, 3],
+    "qwen38_27b_tree": [0, 7],
+    "qwen38_27b_throughput": [0, 63],
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_size_sampled(dev, orc, name):
+    inp = make_inputs(CONFIGS[name])
+    _say(f"[full] {name}: generated inputs")
+    g = _gpu(inp)
+    _say(f"[full] {name}: GPU done, checking blocks {FULL[name]}")
+    reps = check(orc, inp, g, blocks=FULL[name])
+    _say(f"[full] {name}: ok {reps}")
+    c = inp.cfg
+    # properties that hold for every block, checked on all of them
+    assert g["tokens"].shape == (c.B, c.n_pred)
+    assert np.all((g["tokens"] >= 0) & (g["tokens"] < c.V))
+    assert np.array_equal(g["candidates"][:, :, 0], g["tokens"])
+    assert np.all(np.diff(g["cand_logits"], axis=-1) <= 0)
+    if inp.reachable is not None:
+        assert np.all(np.isin(g["tokens"], inp.reachable))
+        assert np.all(np.isin(g["candidates"], inp.reachable))
+    if inp.conf_w is not None:
+        first = np.array([next((j for j in range(c.n_pred) if g["conf"][b, j] < np.float32(c.p_min)),
+                               c.n_pred) for b in range(c.B)])
+        assert np.array_equal(first, g["lengths"])
