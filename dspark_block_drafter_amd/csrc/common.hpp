@@ -67,6 +67,15 @@ __device__ __forceinline__ u64 shfl_xor_u64(u64 v, int mask) {
     return ((u64)hi << 32) | lo;
 }
 
+// Per-lane select (lanes set in `lanes` take if_set). Written as one
+// v_cndmask so that a tree of them is not folded back into an indexed array
+// access (which the compiler would then place in LDS or scratch).
+__device__ __forceinline__ float lane_select(float if_set, float if_clear, u64 lanes) {
+    float r;
+    asm volatile("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(if_clear), "v"(if_set), "s"(lanes));
+    return r;
+}
+
 // Insert `key` into the descending list `list[0..K)`, keeping the K largest.
 template <int K>
 __device__ __forceinline__ void topk_insert(u64 (&list)[K], u64 key) {
@@ -78,5 +87,36 @@ __device__ __forceinline__ void topk_insert(u64 (&list)[K], u64 key) {
         key = lo;
     }
 }
+
+// ---- direct-to-LDS pipelines ----------------------------------------------
+// global_load_lds_dwordx4 writes each lane's 16 bytes to LDS slot base + lane;
+// completion is tracked by vmcnt, so waits and barriers are explicit (a
+// workgroup fence would drain every load in flight).
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Wait until at most `newer` stages of LW loads each are still in flight
+// (newer <= D; the immediate has to be a compile-time constant).
+template <int LW, int D>
+__device__ __forceinline__ void wait_stages(int newer) {
+    if constexpr (D == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (newer >= D) wait_vmcnt<D * LW>();
+        else wait_stages<LW, D - 1>(newer);
+    }
+}
+
+__device__ __forceinline__ void block_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
 
 }  // namespace dspark

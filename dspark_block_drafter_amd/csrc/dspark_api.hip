@@ -90,6 +90,7 @@ int run_chain(const float* logits, const void* hidden, int hidden_dtype, const u
     c.winners = reinterpret_cast<unsigned long long*>(ws + wl.winners_off);
     c.partials = top_k > 1 ? reinterpret_cast<unsigned long long*>(ws + wl.partials_off) : nullptr;
     c.flags = reinterpret_cast<uint32_t*>(ws);
+    c.lengths = lengths;
     c.B = B;
     c.V = V;
     c.r = r;

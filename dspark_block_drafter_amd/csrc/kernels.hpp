@@ -19,9 +19,21 @@ struct GemmArgs {
 hipError_t launch_lmhead_gemm(const GemmArgs& a, bool hidden_f32, hipStream_t stream);
 
 // ---- Markov chain -----------------------------------------------------------
-// Columns of the vocabulary handled by one workgroup of a chain step.
-constexpr int kChainTileV = 512;
-inline int chain_workgroups(int V) { return (V + kChainTileV - 1) / kChainTileV; }
+// Chain step geometry. With V % 4 == 0 the pipelined kernel runs at most
+// kChainMaxWGs workgroups (one per CU), each streaming a contiguous range of
+// kChainTile-column tiles; otherwise the direct kernel runs one workgroup per
+// kChainTileV columns.
+constexpr int kChainTile = 64;
+constexpr int kChainMaxWGs = 256;
+constexpr int kChainTileV = 128;
+inline bool chain_pipelined(int V) { return (V & 3) == 0; }
+inline int chain_workgroups(int V) {
+    if (chain_pipelined(V)) {
+        const int nt = (V + kChainTile - 1) / kChainTile;
+        return nt < kChainMaxWGs ? nt : kChainMaxWGs;
+    }
+    return (V + kChainTileV - 1) / kChainTileV;
+}
 
 struct ChainArgs {
     const float* logits;       // [B * n_pred, V]
@@ -31,6 +43,7 @@ struct ChainArgs {
     unsigned long long* winners;   // [n_pred, B] running argmax keys
     unsigned long long* partials;  // [n_pred, B, nwg, top_k] per-workgroup top-k keys (top_k > 1)
     uint32_t* flags;
+    int32_t* lengths;          // [B], set to n_pred here, cut by the confidence head later
     int B, V, r, n_pred, top_k, nwg;
 };
 hipError_t launch_chain_init(const ChainArgs& a, hipStream_t stream);

@@ -25,6 +25,58 @@ namespace {
 
 constexpr int BK = 64;
 
+// Epilogue shared by the GEMM variants: + bias, fp32 store of the wave's
+// FM x FN accumulator blocks. Per register, lanes 0-31 and 32-63 write 32
+// consecutive columns of two rows (two whole 128-byte lines). Stores are
+// non-temporal: the logits are streamed out once and should not evict the
+// lm_head / hidden tiles from L2. The bias is read once per column before any
+// store, and tiles that lie wholly inside the matrix store without predicates.
+template <int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x16 (&acc)[BM / WM / 32][BN / WN / 32],
+                                           int m0, int n0, int wm, int wn, int lane) {
+    constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
+    const int M = a.M, N = a.N;
+    const int lrow = lane & 31;
+    float bn[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int n = n0 + wn * TN + j * 32 + lrow;
+        bn[j] = (a.bias != nullptr && n < N) ? a.bias[n] : 0.0f;
+    }
+    // The bias loads must be complete before the first store: otherwise the
+    // wait inserted for them also waits for every store issued so far.
+    __builtin_amdgcn_s_waitcnt(0);
+    if (m0 + BM <= M && n0 + BN <= N) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int mb = m0 + wm * TM + i * 32;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                float* col = a.out + (n0 + wn * TN + j * 32 + lrow);
+#pragma unroll
+                for (int g = 0; g < 16; ++g)
+                    __builtin_nontemporal_store(acc[i][j][g] + bn[j], col + (long)(mb + acc_row(g, lane)) * N);
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int mb = m0 + wm * TM + i * 32;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int n = n0 + wn * TN + j * 32 + lrow;
+            float* col = a.out + n;
+#pragma unroll
+            for (int g = 0; g < 16; ++g) {
+                const int m = mb + acc_row(g, lane);
+                if (m < M && n < N)
+                    __builtin_nontemporal_store(acc[i][j][g] + bn[j], col + (long)m * N);
+            }
+        }
+    }
+}
+
 template <bool F32A>
 __device__ __forceinline__ u32x4 load_a_chunk(const void* base, long elem, bool valid) {
     if (!valid) return u32x4{0u, 0u, 0u, 0u};
@@ -38,7 +90,7 @@ __device__ __forceinline__ u32x4 load_a_chunk(const void* base, long elem, bool 
     }
 }
 
-template <int BM, int BN, int WM, int WN, bool F32A>
+template <int BM, int BN, int WM, int WN, bool F32A, bool KFULL>
 __global__ __launch_bounds__(64 * WM * WN) void lmhead_gemm(GemmArgs a) {
     constexpr int NT = 64 * WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
@@ -61,51 +113,47 @@ __global__ __launch_bounds__(64 * WM * WN) void lmhead_gemm(GemmArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
 
-    // Global-load descriptors (fixed for the whole K loop).
-    long a_off[AC];
-    bool a_ok[AC];
-    int a_ch[AC], a_slot[AC];
+    // Global-load descriptors, fixed for the whole K loop. Rows past M / N are
+    // clamped onto the last valid row: they load real data whose products
+    // land only in output rows / columns that are never stored.
+    long a_off[AC], b_off[BC];
+    int a_ch[AC], b_ch[BC], a_slot[AC], b_slot[BC];
 #pragma unroll
     for (int c = 0; c < AC; ++c) {
         const int id = tid + c * NT, row = id >> 3, ch = id & 7;
-        const int m = m0 + row;
-        a_ok[c] = m < M;
-        const int mm = a_ok[c] ? m : 0;
-        const long hrow = (long)(mm / a.n_pred) * a.L + a.i_first + mm % a.n_pred;
+        const int m = min(m0 + row, M - 1);
+        const long hrow = (long)(m / a.n_pred) * a.L + a.i_first + m % a.n_pred;
         a_off[c] = hrow * K + ch * 8;
         a_ch[c] = ch;
         a_slot[c] = row * 8 + (ch ^ (row & 7));
     }
-    long b_off[BC];
-    bool b_ok[BC];
-    int b_ch[BC], b_slot[BC];
 #pragma unroll
     for (int c = 0; c < BC; ++c) {
         const int id = tid + c * NT, row = id >> 3, ch = id & 7;
-        const int n = n0 + row;
-        b_ok[c] = n < N;
-        b_off[c] = (long)(b_ok[c] ? n : 0) * K + ch * 8;
+        b_off[c] = (long)min(n0 + row, N - 1) * K + ch * 8;
         b_ch[c] = ch;
         b_slot[c] = row * 8 + (ch ^ (row & 7));
     }
 
-    u32x4 ra[AC], rb[BC];
-    auto gload = [&](int k0) {
+    // Two register stages: tile t is staged in set t % 2 and LDS buffer t % 2,
+    // so the loads of tile t + 2 are in flight while tile t is multiplied.
+    u32x4 ra[2][AC], rb[2][BC];
+    auto gload = [&](int set, int k0) {
 #pragma unroll
         for (int c = 0; c < AC; ++c)
-            ra[c] = load_a_chunk<F32A>(a.hidden, a_off[c] + k0, a_ok[c] && (k0 + a_ch[c] * 8 < K));
+            ra[set][c] = load_a_chunk<F32A>(a.hidden, a_off[c] + k0, KFULL || k0 + a_ch[c] * 8 < K);
 #pragma unroll
         for (int c = 0; c < BC; ++c) {
-            const bool ok = b_ok[c] && (k0 + b_ch[c] * 8 < K);
-            rb[c] = ok ? *reinterpret_cast<const u32x4*>(a.lm_head + b_off[c] + k0)
-                       : u32x4{0u, 0u, 0u, 0u};
+            const bool ok = KFULL || k0 + b_ch[c] * 8 < K;
+            rb[set][c] = ok ? *reinterpret_cast<const u32x4*>(a.lm_head + b_off[c] + k0)
+                            : u32x4{0u, 0u, 0u, 0u};
         }
     };
-    auto lstore = [&](int buf) {
+    auto lstore = [&](int set, int buf) {
 #pragma unroll
-        for (int c = 0; c < AC; ++c) sA[buf][a_slot[c]] = ra[c];
+        for (int c = 0; c < AC; ++c) sA[buf][a_slot[c]] = ra[set][c];
 #pragma unroll
-        for (int c = 0; c < BC; ++c) sB[buf][b_slot[c]] = rb[c];
+        for (int c = 0; c < BC; ++c) sB[buf][b_slot[c]] = rb[set][c];
     };
 
     f32x16 acc[FM][FN];
@@ -114,15 +162,8 @@ __global__ __launch_bounds__(64 * WM * WN) void lmhead_gemm(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
-    const int nK = (K + BK - 1) / BK;
-    gload(0);
-    lstore(0);
-    __syncthreads();
-
     const int lrow = lane & 31, lhalf = lane >> 5;
-    for (int kt = 0; kt < nK; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nK) gload((kt + 1) * BK);
+    auto mma = [&](int buf) {
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
             const int ch = ks * 2 + lhalf;
@@ -130,38 +171,169 @@ __global__ __launch_bounds__(64 * WM * WN) void lmhead_gemm(GemmArgs a) {
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
                 const int row = wm * TM + i * 32 + lrow;
-                fa[i] = sA[cur][row * 8 + (ch ^ (row & 7))];
+                fa[i] = sA[buf][row * 8 + (ch ^ (row & 7))];
             }
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 const int row = wn * TN + j * 32 + lrow;
-                fb[j] = sB[cur][row * 8 + (ch ^ (row & 7))];
+                fb[j] = sB[buf][row * 8 + (ch ^ (row & 7))];
             }
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16(fa[i], fb[j], acc[i][j]);
         }
-        if (kt + 1 < nK) lstore(cur ^ 1);
+    };
+
+    const int nK = (K + BK - 1) / BK;
+    gload(0, 0);
+    lstore(0, 0);
+    if (nK > 1) gload(1, BK);
+    __syncthreads();
+
+    // Iteration kt: multiply tile kt (LDS buffer kt % 2); load tile kt + 2
+    // into register set kt % 2; stage tile kt + 1 (set (kt+1) % 2) into the
+    // other LDS buffer. Unrolled by two so that the register sets are static.
+    for (int kt = 0; kt < nK; kt += 2) {
+        if (kt + 2 < nK) gload(0, (kt + 2) * BK);
+        mma(0);
+        if (kt + 1 < nK) lstore(1, 1);
+        __syncthreads();
+        if (kt + 1 >= nK) break;
+        if (kt + 3 < nK) gload(1, (kt + 3) * BK);
+        mma(1);
+        if (kt + 2 < nK) lstore(0, 0);
         __syncthreads();
     }
 
-    // Epilogue: + bias, fp32 store. Lanes 0-31 / 32-63 write 32 consecutive
-    // columns of two rows per register: two full 128-byte lines per store.
+    store_tile<BM, BN, WM, WN>(a, acc, m0, n0, wm, wn, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Direct-to-LDS pipeline (bf16 hidden, K % 32 == 0).
+//
+// K advances 32 at a time through an NS-deep ring of LDS stages filled by
+// global_load_lds_dwordx4 (each lane's 16 bytes land at LDS slot base + lane,
+// no register staging), so NS - 1 stages of loads stay in flight while one is
+// multiplied. A stage holds 64-byte rows (4 chunks of 16 B); chunk c of row r
+// sits in physical slot c ^ h(r), h(r) = ((r>>1 ^ r>>3) & 1) | ((r>>2 & 1) << 1),
+// which spreads the same chunk of any 8 (32-bank view) or 16 (64-bank view)
+// consecutive rows over distinct banks. The permutation is applied on the
+// global side: the lane that owns slot p fetches the chunk that belongs there.
+// Barriers are raw s_barrier with explicit vmcnt waits: a workgroup fence
+// would drain every load in flight.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int swz(int row) {
+    return (((row >> 1) ^ (row >> 3)) & 1) | (((row >> 2) & 1) << 1);
+}
+
+
+template <int BM, int BN, int WM, int WN, int NS>
+__global__ __launch_bounds__(64 * WM * WN) void lmhead_gemm_dma(GemmArgs a) {
+    constexpr int NW = WM * WN;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int IA = BM / 16, IB = BN / 16;     // 1 KB wave-loads per stage
+    constexpr int LW = (IA + IB) / NW;            // loads per wave per stage
+    constexpr int BKS = 32;
+    static_assert((IA + IB) % NW == 0, "stage loads must split evenly over waves");
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
+    static_assert(NS >= 2 && (NS - 2) * LW < 64, "pipeline depth");
+
+    // One ring for both operands: stage s holds A rows at slots [0, 4*BM) and
+    // lm_head rows at [4*BM, 4*(BM+BN)).
+    __shared__ u32x4 smem[NS][(BM + BN) * 4];
+
+    const int M = a.M, N = a.N, K = a.K;
+    const int nMT = (M + BM - 1) / BM, nNT = (N + BN - 1) / BN, T = nMT * nNT;
+    const int bid = blockIdx.x;
+    const int sid = (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
+    const int m0 = (sid % nMT) * BM, n0 = (sid / nMT) * BN;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+
+    // This lane's source of each of its LW loads per stage (k offset 0).
+    const uint16_t* src[LW];
+    int dst[LW];        // first slot of the wave's 64-slot destination in a stage
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-        const int n = n0 + wn * TN + j * 32 + lrow;
-        if (n >= N) continue;
-        const float bn = a.bias ? a.bias[n] : 0.0f;
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-#pragma unroll
-            for (int g = 0; g < 16; ++g) {
-                const int m = m0 + wm * TM + i * 32 + acc_row(g, lane);
-                if (m < M) a.out[(long)m * N + n] = acc[i][j][g] + bn;
-            }
+    for (int i = 0; i < LW; ++i) {
+        const int inst = wave + i * NW;
+        const int slot = (inst < IA ? inst : inst - IA) * 64 + lane;
+        const int row = slot >> 2, c = (slot & 3) ^ swz(row);
+        if (inst < IA) {
+            const int m = min(m0 + row, M - 1);
+            const long hrow = (long)(m / a.n_pred) * a.L + a.i_first + m % a.n_pred;
+            src[i] = static_cast<const uint16_t*>(a.hidden) + hrow * K + c * 8;
+            dst[i] = (inst * 64);
+        } else {
+            src[i] = a.lm_head + (long)min(n0 + row, N - 1) * K + c * 8;
+            dst[i] = BM * 4 + (inst - IA) * 64;
         }
     }
+    auto issue = [&](int stage, int k0) {
+#pragma unroll
+        for (int i = 0; i < LW; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(src[i] + k0), (lds_ptr)&smem[stage][dst[i]],
+                                             16, 0, 0);
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+
+    const int lrow = lane & 31, lhalf = lane >> 5;
+    auto mma = [&](int stage) {
+#pragma unroll
+        for (int ks = 0; ks < BKS / 16; ++ks) {
+            const int ch = ks * 2 + lhalf;
+            u32x4 fa[FM], fb[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int row = wm * TM + i * 32 + lrow;
+                fa[i] = smem[stage][row * 4 + (ch ^ swz(row))];
+            }
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int row = wn * TN + j * 32 + lrow;
+                fb[j] = smem[stage][(BM + row) * 4 + (ch ^ swz(row))];
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16(fa[i], fb[j], acc[i][j]);
+        }
+    };
+
+    const int nK = K / BKS;
+#pragma unroll
+    for (int t = 0; t < NS - 1; ++t)
+        if (t < nK) issue(t, t * BKS);
+
+    int stage = 0;
+    for (int kt = 0; kt < nK; ++kt) {
+        // Tile kt must have landed: at most min(NS-2, nK-1-kt) newer tiles may still fly.
+        wait_stages<LW, NS - 2>(min(NS - 2, nK - 1 - kt));
+        block_barrier();  // every wave's part of tile kt is in LDS; stage kt-1 is free
+        const int kn = kt + NS - 1;
+        if (kn < nK) issue(kn % NS, kn * BKS);
+        mma(stage);
+        stage = stage + 1 == NS ? 0 : stage + 1;
+    }
+
+    store_tile<BM, BN, WM, WN>(a, acc, m0, n0, wm, wn, lane);
+}
+
+template <int BM, int BN, int WM, int WN, int NS>
+hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
+    const long tiles = (long)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+    if (tiles > 0x7fffffffL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((lmhead_gemm_dma<BM, BN, WM, WN, NS>), dim3((unsigned)tiles),
+                       dim3(64 * WM * WN), 0, s, a);
+    return hipGetLastError();
 }
 
 template <int BM, int BN, int WM, int WN>
@@ -169,17 +341,27 @@ hipError_t launch_cfg(const GemmArgs& a, bool f32, hipStream_t s) {
     const long tiles = (long)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     if (tiles > 0x7fffffffL) return hipErrorInvalidValue;
     dim3 grid((unsigned)tiles), block(64 * WM * WN);
-    if (f32)
-        hipLaunchKernelGGL((lmhead_gemm<BM, BN, WM, WN, true>), grid, block, 0, s, a);
+    const bool kfull = a.K % BK == 0;
+    if (f32 && kfull)
+        hipLaunchKernelGGL((lmhead_gemm<BM, BN, WM, WN, true, true>), grid, block, 0, s, a);
+    else if (f32)
+        hipLaunchKernelGGL((lmhead_gemm<BM, BN, WM, WN, true, false>), grid, block, 0, s, a);
+    else if (kfull)
+        hipLaunchKernelGGL((lmhead_gemm<BM, BN, WM, WN, false, true>), grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL((lmhead_gemm<BM, BN, WM, WN, false>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((lmhead_gemm<BM, BN, WM, WN, false, false>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_lmhead_gemm(const GemmArgs& a, bool hidden_f32, hipStream_t stream) {
-    if (a.M > 128) return launch_cfg<256, 256, 2, 4>(a, hidden_f32, stream);
+    if (!hidden_f32 && a.K % 32 == 0) {
+        if (a.M > 128) return launch_dma<256, 256, 2, 4, 4>(a, stream);
+        if (a.M > 32) return launch_dma<128, 128, 2, 2, 6>(a, stream);
+        return launch_dma<32, 128, 1, 2, 6>(a, stream);
+    }
+    // fp32 hidden states or K not a multiple of 32: register-staged kernel
     if (a.M > 32) return launch_cfg<128, 128, 2, 2>(a, hidden_f32, stream);
     return launch_cfg<32, 128, 1, 4>(a, hidden_f32, stream);
 }

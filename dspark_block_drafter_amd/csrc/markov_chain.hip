@@ -10,10 +10,12 @@
 // speculation", description).
 //
 // One launch per slot j. A workgroup owns kChainTileV vocabulary columns for
-// up to 64 blocks: it gathers the rank-r rows markov_w1[prev_b] (the MFMA B
-// operand, kept in registers), streams markov_w2 rows (the A operand) and
-// computes the [v x b] bias tile on the bf16 MFMA, adds the logits of slot j
-// and keeps a running top-k per block in registers. The 32x32 accumulator
+// up to 64 blocks. Before it needs them it stages, with coalesced
+// direct-to-LDS loads, the markov_w2 rows of its columns and the slot-j
+// logits of its blocks; meanwhile it gathers the rank-r rows
+// markov_w1[prev_b] (the MFMA B operand, kept in registers). The [v x b]
+// bias tile is one bf16 MFMA product per 32 columns; the logits are added and
+// every lane keeps a running top-k for its block. The 32x32 accumulator
 // layout gives every lane a single block b and 16 vocabulary ids, so the
 // per-lane lists see their ids in increasing order. Lists are merged across
 // the two lanes that share b, then across the four waves through LDS; the
@@ -28,28 +30,25 @@ namespace dspark {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kVBlocksPerWave = kChainTileV / (kWaves * 32);
-static_assert(kVBlocksPerWave * kWaves * 32 == kChainTileV, "tile split");
+static_assert(kChainTileV == kWaves * 32, "one 32-column block per wave");
 
-__global__ __launch_bounds__(256) void chain_init(u64* winners, int n, uint32_t* flags) {
+__global__ __launch_bounds__(256) void chain_init(u64* winners, int n, uint32_t* flags,
+                                                  int32_t* lengths, int B, int n_pred) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) winners[i] = 0ull;
+    if (i < B) lengths[i] = n_pred;
     if (i == 0) *flags = 0u;
 }
 
-// NB: 32-wide block groups per workgroup; KL: per-lane list length (>= top_k);
-// RS: 16-wide k steps covering the rank (r <= 16 * RS, zero padded).
-template <int NB, int KL, int RS>
-__global__ __launch_bounds__(256) void chain_step(ChainArgs a, int j) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int lrow = lane & 31, lhalf = lane >> 5;
-    const int wg = blockIdx.x;
-    const int bbase = blockIdx.y * NB * 32;
-    const int B = a.B, V = a.V, r = a.r;
+// ---- pieces shared by the two step kernels ----------------------------------
 
-    // Gathered markov_w1 rows of each lane's block: MFMA B operand.
-    u32x4 u[NB][RS];
-    int bl[NB];
+// prev_b for slot j (anchor, or the previous slot's argmax) and the lane's
+// share of markov_w1[prev_b] as MFMA B operand: u[nb][s] holds
+// W1[prev][16 s + 8 (lane / 32) .. + 8] for block bbase + 32 nb + lane % 32.
+template <int NB, int RS>
+__device__ __forceinline__ void gather_w1(const ChainArgs& a, int j, int bbase, int lrow, int lhalf,
+                                          u32x4 (&u)[NB][RS], int (&bl)[NB]) {
+    const int B = a.B, V = a.V, r = a.r;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         const int b = bbase + nb * 32 + lrow;
@@ -70,6 +69,313 @@ __global__ __launch_bounds__(256) void chain_step(ChainArgs a, int j) {
                            : u32x4{0u, 0u, 0u, 0u};
         }
     }
+}
+
+// Merge the per-lane lists of a workgroup into one list per block and publish
+// it: partial list (top_k > 1) and atomicMax on the slot's argmax word.
+template <int NB, int KL>
+__device__ __forceinline__ void publish(const ChainArgs& a, int j, int bbase, u64 (&list)[NB][KL],
+                                        u64 (*s_list)[NB * 32][KL]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lrow = lane & 31, lhalf = lane >> 5;
+    // the two lanes that hold the same block (lane, lane ^ 32)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        u64 other[KL];
+#pragma unroll
+        for (int i = 0; i < KL; ++i) other[i] = shfl_xor_u64(list[nb][i], 32);
+#pragma unroll
+        for (int i = 0; i < KL; ++i) topk_insert<KL>(list[nb], other[i]);
+    }
+    if (lhalf == 0) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int i = 0; i < KL; ++i) s_list[wave][nb * 32 + lrow][i] = list[nb][i];
+    }
+    __syncthreads();
+    const int t = threadIdx.x;
+    const int B = a.B;
+    if (t < NB * 32) {
+        const int b = bbase + t;
+        if (b < B) {
+            u64 m[KL];
+#pragma unroll
+            for (int i = 0; i < KL; ++i) m[i] = s_list[0][t][i];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w)
+#pragma unroll
+                for (int i = 0; i < KL; ++i) topk_insert<KL>(m, s_list[w][t][i]);
+            if (a.top_k > 1) {
+                u64* p = a.partials + (((long)j * B + b) * a.nwg + blockIdx.x) * a.top_k;
+#pragma unroll
+                for (int i = 0; i < KL; ++i)
+                    if (i < a.top_k) p[i] = m[i];
+            }
+            if (m[0] != 0ull) atomicMax(a.winners + (long)j * B + b, m[0]);
+        }
+    }
+}
+
+// ---- step kernel for V % 4 == 0: operands staged through LDS -----------------
+
+// Swizzle of a staged row of R 16-byte chunks: chunk c of row `row` is stored
+// at c ^ swz_rows<R>(row). MFMA operand reads take one chunk of 32
+// consecutive rows; the permutation spreads any 8 (32-bank view) or 16
+// (64-bank view) consecutive rows over distinct banks.
+template <int R>
+__device__ __forceinline__ int swz_rows(int row) {
+    if constexpr (R >= 16) return row & 15;
+    else if constexpr (R == 8) return (row ^ (row >> 3)) & 7;
+    else if constexpr (R == 4) return (((row >> 1) ^ (row >> 3)) & 1) | (((row >> 2) & 1) << 1);
+    else if constexpr (R == 2) return ((row >> 2) ^ (row >> 3)) & 1;
+    else return 0;
+}
+
+// Workgroup g streams the vocabulary range of tiles [t0, t1) (kChainTile
+// columns each) for up to 64 blocks. Every tile's markov_w2 rows and slot-j
+// logits go through an NS-deep ring of LDS stages filled by direct-to-LDS
+// loads, so NS - 1 tiles are in flight while one is scored. Wave w scores the
+// 32 columns (w % 2) of the tile for block group w / 2. The workgroup
+// publishes once per slot, after its whole range.
+template <int NB, int KL, int RS, int NS>
+__global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
+    constexpr int TS = kChainTile;          // columns per tile (two 32-column MFMA blocks)
+    constexpr int WR = 2 * RS;              // 16-byte chunks per staged markov_w2 row
+    constexpr int WRd = WR > 0 ? WR : 1;    // (divisor; only used when RS > 0)
+    constexpr int LR = TS / 4;              // 16-byte chunks per staged logits row
+    constexpr int W_SLOTS = RS > 0 ? TS * WR : 0;
+    constexpr int L_SLOTS = NB * 32 * LR;
+    constexpr int STAGE = W_SLOTS + L_SLOTS;
+    constexpr int W_INST = W_SLOTS / 64, L_INST = L_SLOTS / 64;
+    constexpr int LW = (W_INST + L_INST) / kWaves;  // loads per wave per tile
+    static_assert(TS == 64 && (W_INST + L_INST) % kWaves == 0, "tile loads must split over waves");
+    static_assert(NS >= 2 && (NS - 2) * LW < 64, "pipeline depth");
+    static_assert(kWaves * KL * NB * 32 * 8 <= NS * STAGE * 16, "list merge reuses the ring");
+    __shared__ u32x4 ring[NS][STAGE];
+    // Last-entry score of each wave's lists, per block: a lower bound of the
+    // block's KL-th best score in this workgroup, shared with the wave that
+    // scores the other 32 columns of the same blocks.
+    __shared__ float s_thr[kWaves][32];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lrow = lane & 31, lhalf = lane >> 5;
+    const int vb = wave & 1, nbw = wave >> 1;        // this wave's 32-column block / block group
+    const int bbase = blockIdx.y * NB * 32;
+    const int B = a.B, V = a.V, r = a.r;
+    const int nT = (V + TS - 1) / TS, G = gridDim.x, g = blockIdx.x;
+    const int t0 = (int)((long)nT * g / G), t1 = (int)((long)nT * (g + 1) / G);
+    const int n = t1 - t0;
+
+    // This lane's fixed part of each of its LW loads per tile.
+    const char* src[LW];
+    int dst[LW];
+    long step[LW];   // bytes to advance per tile
+#pragma unroll
+    for (int i = 0; i < LW; ++i) {
+        const int inst = wave + i * kWaves;
+        if (inst < W_INST) {
+            const int slot = inst * 64 + lane, row = slot / WRd;
+            const int c = (slot % WRd) ^ swz_rows<WR>(row);
+            const int k = c * 8 < r ? c * 8 : 0;   // rank padding: any valid chunk
+            src[i] = reinterpret_cast<const char*>(a.w2 + (long)row * r + k);
+            step[i] = (long)TS * r * 2;
+            dst[i] = inst * 64;
+        } else {
+            const int slot = (inst - W_INST) * 64 + lane, row = slot / LR;
+            const int c = (slot % LR) ^ swz_rows<LR>(row);
+            const int b = min(bbase + row, B - 1);
+            src[i] = reinterpret_cast<const char*>(a.logits + ((long)b * a.n_pred + j) * V + 4 * c);
+            step[i] = (long)TS * 4;
+            dst[i] = W_SLOTS + (inst - W_INST) * 64;
+        }
+    }
+    // Columns past V: markov_w2 rows are clamped to row V-1, logits to the
+    // last 16-byte chunk of the row; such columns are never scored.
+    auto issue = [&](int st, int t) {
+        const int v0 = t * TS;
+#pragma unroll
+        for (int i = 0; i < LW; ++i) {
+            const char* p = src[i] + (long)t * step[i];
+            if (i * kWaves + wave < W_INST) {
+                const int row = ((i * kWaves + wave) * 64 + lane) / WRd;
+                if (v0 + row >= V) p -= (long)(v0 + row - (V - 1)) * r * 2;
+            } else {
+                const int slot = ((i * kWaves + wave) - W_INST) * 64 + lane;
+                const int c = (slot % LR) ^ swz_rows<LR>(slot / LR);
+                if (v0 + 4 * c > V - 4) p -= (long)(v0 + 4 * c - (V - 4)) * 4;
+            }
+            __builtin_amdgcn_global_load_lds((const void*)p, (lds_ptr)&ring[st][dst[i]], 16, 0, 0);
+        }
+    };
+
+    // Previous token of this lane's block (anchor, or the last slot's argmax).
+    const int bme = bbase + nbw * 32 + lrow;
+    int prev = 0;
+    if (bme < B && nbw < NB) {
+        prev = (j == 0) ? a.anchors[bme] : key_id(a.winners[(long)(j - 1) * B + bme]);
+        if (prev < 0 || prev >= V) {
+            if (j == 0 && vb == 0) atomicOr(a.flags, 1u);
+            prev = 0;
+        }
+    }
+    // First NS - 1 tiles in flight, then the markov_w1 rows of prev (MFMA B
+    // operand). One full wait before the loop: the loop then only ever waits
+    // for ring stages (a register load still in flight there would make every
+    // iteration drain the whole ring).
+#pragma unroll
+    for (int t = 0; t < NS - 2; ++t)
+        if (t < n) issue(t, t0 + t);
+    u32x4 u[RS > 0 ? RS : 1];
+#pragma unroll
+    for (int s = 0; s < RS; ++s) {
+        const int k0 = s * 16 + lhalf * 8;
+        u[s] = (bme < B && nbw < NB && k0 < r)
+                   ? *reinterpret_cast<const u32x4*>(a.w1 + (long)prev * r + k0)
+                   : u32x4{0u, 0u, 0u, 0u};
+    }
+    wait_vmcnt<0>();
+
+    // MFMA runs on whole waves: only the wave-uniform part of the condition may
+    // guard it; blocks past B are masked at the inserts.
+    const bool wave_on = nbw < NB;
+    const bool active = wave_on && bme < B;
+
+    u64 list[KL];
+#pragma unroll
+    for (int i = 0; i < KL; ++i) list[i] = 0ull;
+    if (lhalf == 0) s_thr[wave][lrow] = -INFINITY;
+
+    int st = 0;
+    for (int it = 0; it < n; ++it) {
+        // Tile it + NS - 2 goes into the stage of tile it - 2, which every wave
+        // finished before passing the previous barrier; issuing it before this
+        // iteration's wait keeps the ring full while slow waves catch up.
+        if (it + NS - 2 < n) issue((st + NS - 2) % NS, t0 + it + NS - 2);
+        wait_stages<LW, NS - 2>(min(NS - 2, n - 1 - it));
+        block_barrier();
+        if (wave_on) {
+            const u32x4* stg = ring[st];
+            const int vrow = vb * 32 + lrow;
+            f32x16 acc = f32x16{};
+#pragma unroll
+            for (int s = 0; s < RS; ++s) {
+                const u32x4 w = stg[vrow * WR + ((2 * s + lhalf) ^ swz_rows<WR>(vrow))];
+                acc = mfma32x32x16(w, u[s], acc);
+            }
+            const int row = nbw * 32 + lrow;
+            const int vt = (t0 + it) * TS + vb * 32;
+            // z[4q + e] is the biased score of column vt + 8q + 4(lane/32) + e.
+            float z[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int c = vb * 8 + 2 * q + lhalf;
+                const f32x4 x = __builtin_bit_cast(
+                    f32x4, stg[W_SLOTS + row * LR + (c ^ swz_rows<LR>(row))]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) z[4 * q + e] = x[e] + acc[4 * q + e];
+            }
+            const int vlane = vt + 4 * lhalf;
+            const bool full = vt + 32 <= V;
+            if (KL == 1 || it == 0 || !full) {
+                // plain inserts (argmax lists, the first tile, the ragged last tile)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int v = vlane + 8 * (e >> 2) + (e & 3);
+                    if (active && v < V) {
+                        const u64 key = make_key(z[e], v);
+                        if (key > list[KL - 1]) topk_insert<KL>(list, key);
+                    }
+                }
+            } else {
+                // Filtered inserts: a score can only enter this lane's list if it
+                // beats the list's last entry, and cannot be among the block's
+                // best KL if it does not beat the last entry of the partner
+                // lane's list either (both lists are subsets of the block's
+                // scores; a lane's ids rise, so ties go to the listed entry).
+                // Hits are inserted in rounds, one per lane per round.
+                float thr = list[KL - 1] != 0ull ? key_score(list[KL - 1]) : -INFINITY;
+                thr = fmaxf(thr, __shfl_xor(thr, 32, kWave));
+                thr = fmaxf(thr, s_thr[wave ^ 1][lrow]);
+                unsigned hits = 0u;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) hits |= (z[e] > thr ? 1u : 0u) << e;
+                if (!active) hits = 0u;
+                while (__any(hits != 0u)) {
+                    if (hits != 0u) {
+                        const int e = __builtin_ctz(hits);
+                        hits &= hits - 1u;
+                        // z[e] by a select tree on the bits of e
+                        const u64 m0 = __builtin_amdgcn_ballot_w64((e & 1) != 0);
+                        const u64 m1 = __builtin_amdgcn_ballot_w64((e & 2) != 0);
+                        const u64 m2 = __builtin_amdgcn_ballot_w64((e & 4) != 0);
+                        const u64 m3 = __builtin_amdgcn_ballot_w64((e & 8) != 0);
+                        float s8[8], s4[4], s2[2];
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) s8[i] = lane_select(z[2 * i + 1], z[2 * i], m0);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) s4[i] = lane_select(s8[2 * i + 1], s8[2 * i], m1);
+#pragma unroll
+                        for (int i = 0; i < 2; ++i) s2[i] = lane_select(s4[2 * i + 1], s4[2 * i], m2);
+                        const float ze = lane_select(s2[1], s2[0], m3);
+                        const u64 key = make_key(ze, vlane + 8 * (e >> 2) + (e & 3));
+                        if (key > list[KL - 1]) topk_insert<KL>(list, key);
+                    }
+                }
+            }
+            if (KL > 1) {
+                // publish this wave's bound for the partner wave's next tile
+                float own = list[KL - 1] != 0ull ? key_score(list[KL - 1]) : -INFINITY;
+                own = fmaxf(own, __shfl_xor(own, 32, kWave));
+                if (lhalf == 0) s_thr[wave][lrow] = own;
+            }
+        }
+        st = st + 1 == NS ? 0 : st + 1;
+    }
+
+    // Merge: the lane pair that holds the same block, then the two waves of
+    // the block group (their lists go through the ring, free by now).
+    {
+        u64 other[KL];
+#pragma unroll
+        for (int i = 0; i < KL; ++i) other[i] = shfl_xor_u64(list[i], 32);
+#pragma unroll
+        for (int i = 0; i < KL; ++i) topk_insert<KL>(list, other[i]);
+    }
+    u64* s_list = reinterpret_cast<u64*>(&ring[0][0]);  // [wave][32][KL]
+    __syncthreads();
+    if (lhalf == 0) {
+#pragma unroll
+        for (int i = 0; i < KL; ++i) s_list[(wave * 32 + lrow) * KL + i] = list[i];
+    }
+    __syncthreads();
+    if (vb == 0 && lhalf == 0 && active) {
+#pragma unroll
+        for (int i = 0; i < KL; ++i) topk_insert<KL>(list, s_list[((wave + 1) * 32 + lrow) * KL + i]);
+        const int b = bme;
+        if (a.top_k > 1) {
+            u64* p = a.partials + (((long)j * B + b) * a.nwg + g) * a.top_k;
+#pragma unroll
+            for (int i = 0; i < KL; ++i)
+                if (i < a.top_k) p[i] = list[i];
+        }
+        if (list[0] != 0ull) atomicMax(a.winners + (long)j * B + b, list[0]);
+    }
+}
+
+// ---- step kernel for any V: operands read straight from global memory --------
+
+template <int NB, int KL, int RS>
+__global__ __launch_bounds__(256) void chain_step_direct(ChainArgs a, int j) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lrow = lane & 31, lhalf = lane >> 5;
+    const int bbase = blockIdx.y * NB * 32;
+    const int B = a.B, V = a.V, r = a.r;
+    __shared__ u64 s_list[kWaves][NB * 32][KL];
+
+    u32x4 u[NB][RS];
+    int bl[NB];
+    gather_w1<NB, RS>(a, j, bbase, lrow, lhalf, u, bl);
 
     u64 list[NB][KL];
 #pragma unroll
@@ -77,11 +383,8 @@ __global__ __launch_bounds__(256) void chain_step(ChainArgs a, int j) {
 #pragma unroll
         for (int i = 0; i < KL; ++i) list[nb][i] = 0ull;
 
-    const bool vec4 = (V & 3) == 0;
-    for (int vb = 0; vb < kVBlocksPerWave; ++vb) {
-        const int v0 = wg * kChainTileV + (wave * kVBlocksPerWave + vb) * 32;
-        if (v0 >= V) break;
-        // markov_w2 rows v0 + lrow: MFMA A operand.
+    const int v0 = blockIdx.x * kChainTileV + wave * 32;
+    if (v0 < V) {
         const int vrow = v0 + lrow;
         u32x4 w[RS];
 #pragma unroll
@@ -103,93 +406,49 @@ __global__ __launch_bounds__(256) void chain_step(ChainArgs a, int j) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int vq = v0 + 8 * q + 4 * lhalf;
-                float z[4];
-                if (vec4 && vq + 3 < V) {
-                    const f32x4 x = *reinterpret_cast<const f32x4*>(row + vq);
-                    z[0] = x[0]; z[1] = x[1]; z[2] = x[2]; z[3] = x[3];
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) z[e] = (vq + e < V) ? row[vq + e] : 0.0f;
-                }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int v = vq + e;
                     if (v < V) {
-                        const u64 key = make_key(z[e] + acc[4 * q + e], v);
+                        const u64 key = make_key(row[v] + acc[4 * q + e], v);
                         if (key > list[nb][KL - 1]) topk_insert<KL>(list[nb], key);
                     }
                 }
             }
         }
     }
-
-    // Merge the two lanes that hold the same block (lane, lane ^ 32).
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        u64 other[KL];
-#pragma unroll
-        for (int i = 0; i < KL; ++i) other[i] = shfl_xor_u64(list[nb][i], 32);
-#pragma unroll
-        for (int i = 0; i < KL; ++i) topk_insert<KL>(list[nb], other[i]);
-    }
-
-    // Merge across waves through LDS.
-    __shared__ u64 s_list[kWaves][NB * 32][KL];
-    if (lhalf == 0) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int i = 0; i < KL; ++i) s_list[wave][nb * 32 + lrow][i] = list[nb][i];
-    }
-    __syncthreads();
-    const int t = threadIdx.x;
-    if (t < NB * 32) {
-        const int b = bbase + t;
-        if (b < B) {
-            u64 m[KL];
-#pragma unroll
-            for (int i = 0; i < KL; ++i) m[i] = s_list[0][t][i];
-#pragma unroll
-            for (int w2 = 1; w2 < kWaves; ++w2)
-#pragma unroll
-                for (int i = 0; i < KL; ++i) topk_insert<KL>(m, s_list[w2][t][i]);
-            if (a.top_k > 1) {
-                u64* p =
-                    a.partials + (((long)j * B + b) * a.nwg + wg) * a.top_k;
-#pragma unroll
-                for (int i = 0; i < KL; ++i)
-                    if (i < a.top_k) p[i] = m[i];
-            }
-            if (m[0] != 0ull) atomicMax(a.winners + (long)j * B + b, m[0]);
-        }
-    }
+    publish<NB, KL>(a, j, bbase, list, s_list);
 }
 
-// Final assembly, one workgroup per block: tokens and candidates of every
-// slot, then the confidence head and the prefix cut.
+// ---- final assembly: one workgroup per (slot, block) --------------------------
+
+// Candidates of slot j of block b from the per-workgroup partial lists, then
+// the confidence of that slot; lengths[b] (preset to n_pred) is lowered to j
+// when conf < p_min, so it ends at the first such slot (llama.cpp commit
+// 6fed9f6, "spec: add confidence-based draft pruning for DSpark" and
+// "dspark: fold conf_min into p_min").
 template <int KL>
 __global__ __launch_bounds__(256) void finalize(FinalArgs a) {
-    const int b = blockIdx.x;
+    const int j = blockIdx.x, b = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int B = a.B, n = a.n_pred, k = a.top_k;
+    const long o = (long)b * n + j;
+    const u64 win = a.winners[(long)j * B + b];
+    __shared__ u64 s_list[kWaves][KL];
 
-    for (int j = wave; j < n; j += kWaves) {
-        const u64 win = a.winners[(long)j * B + b];
-        const long o = (long)b * n + j;
-        if (k == 1) {
-            if (lane == 0) {
-                a.tokens[o] = key_id(win);
-                a.candidates[o] = key_id(win);
-                if (a.cand_logits) a.cand_logits[o] = key_score(win);
-            }
-            continue;
+    if (k == 1) {
+        if (threadIdx.x == 0) {
+            a.tokens[o] = key_id(win);
+            a.candidates[o] = key_id(win);
+            if (a.cand_logits) a.cand_logits[o] = key_score(win);
         }
+    } else {
         u64 list[KL];
 #pragma unroll
         for (int i = 0; i < KL; ++i) list[i] = 0ull;
         const u64* p = a.partials + ((long)j * B + b) * a.nwg * k;
         const int cnt = a.nwg * k;
-        for (int e = lane; e < cnt; e += 64) {
+        for (int e = threadIdx.x; e < cnt; e += 256) {
             const u64 key = p[e];
             if (key > list[KL - 1]) topk_insert<KL>(list, key);
         }
@@ -202,6 +461,15 @@ __global__ __launch_bounds__(256) void finalize(FinalArgs a) {
             for (int i = 0; i < KL; ++i) topk_insert<KL>(list, other[i]);
         }
         if (lane == 0) {
+#pragma unroll
+            for (int i = 0; i < KL; ++i) s_list[wave][i] = list[i];
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w)
+#pragma unroll
+                for (int i = 0; i < KL; ++i) topk_insert<KL>(list, s_list[w][i]);
             a.tokens[o] = key_id(win);
             if (list[0] != win) atomicOr(a.flags, 2u);  // internal consistency check
 #pragma unroll
@@ -214,13 +482,8 @@ __global__ __launch_bounds__(256) void finalize(FinalArgs a) {
         }
     }
 
-    // Confidence head: conf = sigmoid(hidden . conf_w); length = first slot
-    // with conf < p_min (llama.cpp commit 6fed9f6, "spec: add confidence-based
-    // draft pruning for DSpark" and "dspark: fold conf_min into p_min").
-    __shared__ int s_len;
-    if (threadIdx.x == 0) s_len = n;
-    __syncthreads();
-    for (int j = wave; j < n; j += kWaves) {
+    // Confidence head on wave 1 (wave 0 may still be writing candidates).
+    if (wave == 1 % kWaves) {
         float c = 1.0f;
         if (a.conf_w) {
             const long row = (long)b * a.L + a.i_first + j;
@@ -254,38 +517,58 @@ __global__ __launch_bounds__(256) void finalize(FinalArgs a) {
 #pragma unroll
             for (int mask = 32; mask >= 1; mask >>= 1) s += __shfl_xor(s, mask, 64);
             c = 1.0f / (1.0f + expf(-s));
-            if (lane == 0 && c < a.p_min) atomicMin(&s_len, j);
+            if (lane == 0 && c < a.p_min) atomicMin(a.lengths + b, j);
         }
-        if (lane == 0 && a.conf) a.conf[(long)b * n + j] = c;
+        if (lane == 0 && a.conf) a.conf[o] = c;
     }
-    __syncthreads();
-    if (threadIdx.x == 0) a.lengths[b] = s_len;
 }
 
 template <int NB, int KL>
-hipError_t step_rs(const ChainArgs& a, int j, dim3 grid, hipStream_t s) {
+hipError_t step_direct(const ChainArgs& a, int j, dim3 grid, hipStream_t s) {
     const int rs = (a.r + 15) / 16;
-    if (rs <= 1) hipLaunchKernelGGL((chain_step<NB, KL, 1>), grid, dim3(256), 0, s, a, j);
-    else if (rs <= 2) hipLaunchKernelGGL((chain_step<NB, KL, 2>), grid, dim3(256), 0, s, a, j);
-    else if (rs <= 4) hipLaunchKernelGGL((chain_step<NB, KL, 4>), grid, dim3(256), 0, s, a, j);
-    else if (rs <= 8) hipLaunchKernelGGL((chain_step<NB, KL, 8>), grid, dim3(256), 0, s, a, j);
-    else hipLaunchKernelGGL((chain_step<NB, KL, 16>), grid, dim3(256), 0, s, a, j);
+#define DSPARK_STEP(RSV) hipLaunchKernelGGL((chain_step_direct<NB, KL, RSV>), grid, dim3(256), 0, s, a, j);
+    if (rs <= 1) { DSPARK_STEP(1) }
+    else if (rs <= 2) { DSPARK_STEP(2) }
+    else if (rs <= 4) { DSPARK_STEP(4) }
+    else if (rs <= 8) { DSPARK_STEP(8) }
+    else { DSPARK_STEP(16) }
+#undef DSPARK_STEP
+    return hipGetLastError();
+}
+
+template <int NB, int KL>
+hipError_t step_pipe(const ChainArgs& a, int j, dim3 grid, hipStream_t s) {
+    const int rs = (a.r + 15) / 16;
+#define DSPARK_STEP(RSV, NSV) hipLaunchKernelGGL((chain_step_pipe<NB, KL, RSV, NSV>), grid, dim3(256), 0, s, a, j);
+    if (rs == 0) { DSPARK_STEP(0, 4) }
+    else if (rs <= 2) { DSPARK_STEP(2, 4) }
+    else if (rs <= 4) { DSPARK_STEP(4, 4) }
+    else if (rs <= 8) { DSPARK_STEP(8, 4) }
+    else { DSPARK_STEP(16, 3) }
+#undef DSPARK_STEP
     return hipGetLastError();
 }
 
 template <int NB>
-hipError_t step_kl(const ChainArgs& a, int j, dim3 grid, hipStream_t s) {
-    if (a.top_k == 1) return step_rs<NB, 1>(a, j, grid, s);
-    if (a.top_k <= 4) return step_rs<NB, 4>(a, j, grid, s);
-    if (a.top_k <= 8) return step_rs<NB, 8>(a, j, grid, s);
-    return step_rs<NB, 16>(a, j, grid, s);
+hipError_t step_kl(const ChainArgs& a, int j, dim3 grid, bool pipe, hipStream_t s) {
+    if (pipe) {
+        if (a.top_k == 1) return step_pipe<NB, 1>(a, j, grid, s);
+        if (a.top_k <= 4) return step_pipe<NB, 4>(a, j, grid, s);
+        if (a.top_k <= 8) return step_pipe<NB, 8>(a, j, grid, s);
+        return step_pipe<NB, 16>(a, j, grid, s);
+    }
+    if (a.top_k == 1) return step_direct<NB, 1>(a, j, grid, s);
+    if (a.top_k <= 4) return step_direct<NB, 4>(a, j, grid, s);
+    if (a.top_k <= 8) return step_direct<NB, 8>(a, j, grid, s);
+    return step_direct<NB, 16>(a, j, grid, s);
 }
 
 }  // namespace
 
 hipError_t launch_chain_init(const ChainArgs& a, hipStream_t stream) {
-    const int n = a.n_pred * a.B;
-    hipLaunchKernelGGL(chain_init, dim3((n + 255) / 256), dim3(256), 0, stream, a.winners, n, a.flags);
+    const int n = a.n_pred * a.B > a.B ? a.n_pred * a.B : a.B;
+    hipLaunchKernelGGL(chain_init, dim3((n + 255) / 256), dim3(256), 0, stream, a.winners,
+                       a.n_pred * a.B, a.flags, a.lengths, a.B, a.n_pred);
     return hipGetLastError();
 }
 
@@ -294,11 +577,12 @@ hipError_t launch_chain_step(const ChainArgs& a, int j, hipStream_t stream) {
     // markov_w2 tile is read once per step for all of them.
     const int nb = a.B > 32 ? 2 : 1;
     dim3 grid(a.nwg, (a.B + 32 * nb - 1) / (32 * nb));
-    return nb == 2 ? step_kl<2>(a, j, grid, stream) : step_kl<1>(a, j, grid, stream);
+    const bool pipe = chain_pipelined(a.V);
+    return nb == 2 ? step_kl<2>(a, j, grid, pipe, stream) : step_kl<1>(a, j, grid, pipe, stream);
 }
 
 hipError_t launch_finalize(const FinalArgs& a, hipStream_t stream) {
-    dim3 grid(a.B), block(256);
+    dim3 grid(a.n_pred, a.B), block(256);
     if (a.top_k <= 1) hipLaunchKernelGGL(finalize<1>, grid, block, 0, stream, a);
     else if (a.top_k <= 4) hipLaunchKernelGGL(finalize<4>, grid, block, 0, stream, a);
     else if (a.top_k <= 8) hipLaunchKernelGGL(finalize<8>, grid, block, 0, stream, a);

@@ -55,6 +55,10 @@ SMALL = {
     "single_slot": lambda: make_small(1, 1, 32, 33, 8, top_k=1, seed=7),
     "mid_gemm_M33": lambda: make_small(11, 3, 1032, 4097, 32, top_k=2, seed=8),
     "rank256": lambda: make_small(6, 4, 128, 1536, 256, top_k=3, seed=9, w_std=0.2),
+    "dma_mid_M63": lambda: make_small(9, 7, 160, 3001, 16, top_k=2, conf=True, p_min=0.4, seed=18),
+    "dma_big_K32": lambda: make_small(20, 13, 32, 700, 8, top_k=3, seed=19),
+    "dma_big_K96_bonus": lambda: make_small(23, 12, 96, 1000, 24, top_k=1, layout=BONUS_ANCHOR,
+                                             conf=True, p_min=0.5, seed=20),
     "reduced_vocab": lambda: make_small(4, 7, 176, 4096, 64, top_k=4, layout=BONUS_ANCHOR,
                                         reachable=300, conf=True, p_min=0.5, conf_trend=True,
                                         seed=10),
