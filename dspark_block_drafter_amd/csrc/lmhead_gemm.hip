@@ -327,6 +327,132 @@ __global__ __launch_bounds__(64 * WM * WN) void lmhead_gemm_dma(GemmArgs a) {
     store_tile<BM, BN, WM, WN>(a, acc, m0, n0, wm, wn, lane);
 }
 
+// ---------------------------------------------------------------------------
+// Split-ring pipeline for large M (bf16 hidden, K % 64 == 0).
+//
+// K advances 64 at a time: a stage row is one 128-byte line. The two operands
+// get rings sized to their latency: the hidden rows (A) are re-read by every
+// lm_head slab and stay in L2, so two stages suffice; the lm_head rows (B) are
+// read from HBM once, so they get three stages and two of them are always in
+// flight. Per iteration the loads are issued A(kt+1) first, then
+// B(kt+NSB-1), so that the in-order vmcnt wait for A(kt) never has to wait
+// for the newest B loads. Both rings live in one LDS array: with separate
+// arrays the compiler drains every in-flight LDS load before each LDS read.
+// ---------------------------------------------------------------------------
+template <int CH>
+__device__ __forceinline__ int swz_ch(int row) {
+    if constexpr (CH == 8) return (row ^ (row >> 3)) & 7;
+    else return swz(row);
+}
+
+template <int BM, int BN, int WM, int WN, int NSA, int NSB>
+__global__ __launch_bounds__(64 * WM * WN) void lmhead_gemm_split(GemmArgs a) {
+    constexpr int NW = WM * WN;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int BKS = 64, CH = BKS / 8;
+    constexpr int IA = BM * CH / 64, IB = BN * CH / 64;  // 1 KB wave-loads per stage
+    constexpr int LA = IA / NW, LB = IB / NW;
+    static_assert(IA % NW == 0 && IB % NW == 0, "stage loads must split evenly over waves");
+    static_assert(NSA == 2 && NSB >= 2, "ring depths");
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
+    constexpr int BOFF = NSA * BM * CH;
+    __shared__ u32x4 smem[NSA * BM * CH + NSB * BN * CH];
+
+    const int M = a.M, N = a.N, K = a.K;
+    const int nMT = (M + BM - 1) / BM, nNT = (N + BN - 1) / BN, T = nMT * nNT;
+    const int bid = blockIdx.x;
+    const int sid = (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
+    const int m0 = (sid % nMT) * BM, n0 = (sid / nMT) * BN;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+
+    // The lane that owns LDS slot p of a stage fetches the chunk the swizzle
+    // puts there; rows past M / N are clamped (their products are not stored).
+    const uint16_t* srcA[LA];
+    const uint16_t* srcB[LB];
+    int dstA[LA], dstB[LB];
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+        const int inst = wave + i * NW, slot = inst * 64 + lane;
+        const int row = slot / CH, c = (slot % CH) ^ swz_ch<CH>(row);
+        const int m = min(m0 + row, M - 1);
+        const long hrow = (long)(m / a.n_pred) * a.L + a.i_first + m % a.n_pred;
+        srcA[i] = static_cast<const uint16_t*>(a.hidden) + hrow * K + c * 8;
+        dstA[i] = inst * 64;
+    }
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+        const int inst = wave + i * NW, slot = inst * 64 + lane;
+        const int row = slot / CH, c = (slot % CH) ^ swz_ch<CH>(row);
+        srcB[i] = a.lm_head + (long)min(n0 + row, N - 1) * K + c * 8;
+        dstB[i] = inst * 64;
+    }
+    auto issueA = [&](int st, int k0) {
+#pragma unroll
+        for (int i = 0; i < LA; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(srcA[i] + k0),
+                                             (lds_ptr)&smem[st * BM * CH + dstA[i]], 16, 0, 0);
+    };
+    auto issueB = [&](int st, int k0) {
+#pragma unroll
+        for (int i = 0; i < LB; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(srcB[i] + k0),
+                                             (lds_ptr)&smem[BOFF + st * BN * CH + dstB[i]], 16, 0, 0);
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+    const int lrow = lane & 31, lhalf = lane >> 5;
+    auto mma = [&](int stA, int stB) {
+#pragma unroll
+        for (int ks = 0; ks < BKS / 16; ++ks) {
+            const int ch = ks * 2 + lhalf;
+            u32x4 fa[FM], fb[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int row = wm * TM + i * 32 + lrow;
+                fa[i] = smem[stA * BM * CH + row * CH + (ch ^ swz_ch<CH>(row))];
+            }
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int row = wn * TN + j * 32 + lrow;
+                fb[j] = smem[BOFF + stB * BN * CH + row * CH + (ch ^ swz_ch<CH>(row))];
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16(fa[i], fb[j], acc[i][j]);
+        }
+    };
+
+    const int nK = K / BKS;
+    // Prologue order: B(0 .. NSB-3), A(0), B(NSB-2): at kt = 0 only the newest
+    // B stage may still be in flight.
+#pragma unroll
+    for (int t = 0; t < NSB - 2; ++t)
+        if (t < nK) issueB(t, t * BKS);
+    issueA(0, 0);
+    if (NSB - 2 < nK) issueB(NSB - 2, (NSB - 2) * BKS);
+
+    int sA = 0, sB = 0;
+    for (int kt = 0; kt < nK; ++kt) {
+        // Loads issued after A(kt): B(kt + NSB - 2) only, when it exists.
+        if (kt + NSB - 2 < nK) wait_vmcnt<LB>();
+        else wait_vmcnt<0>();
+        block_barrier();  // A(kt), B(kt) landed for every wave; stages of kt-1 are free
+        if (kt + 1 < nK) issueA(sA ^ 1, (kt + 1) * BKS);
+        if (kt + NSB - 1 < nK) issueB((sB + NSB - 1) % NSB, (kt + NSB - 1) * BKS);
+        mma(sA, sB);
+        sA ^= 1;
+        sB = sB + 1 == NSB ? 0 : sB + 1;
+    }
+    store_tile<BM, BN, WM, WN>(a, acc, m0, n0, wm, wn, lane);
+}
+
 template <int BM, int BN, int WM, int WN, int NS>
 hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
     const long tiles = (long)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
@@ -357,6 +483,13 @@ hipError_t launch_cfg(const GemmArgs& a, bool f32, hipStream_t s) {
 
 hipError_t launch_lmhead_gemm(const GemmArgs& a, bool hidden_f32, hipStream_t stream) {
     if (!hidden_f32 && a.K % 32 == 0) {
+        if (a.M > 128 && a.K % 64 == 0) {
+            const long tiles = (long)((a.M + 255) / 256) * ((a.N + 255) / 256);
+            if (tiles > 0x7fffffffL) return hipErrorInvalidValue;
+            hipLaunchKernelGGL((lmhead_gemm_split<256, 256, 2, 4, 2, 3>), dim3((unsigned)tiles),
+                               dim3(512), 0, stream, a);
+            return hipGetLastError();
+        }
         if (a.M > 128) return launch_dma<256, 256, 2, 4, 4>(a, stream);
         if (a.M > 32) return launch_dma<128, 128, 2, 2, 6>(a, stream);
         return launch_dma<32, 128, 1, 2, 6>(a, stream);
