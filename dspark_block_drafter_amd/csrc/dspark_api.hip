@@ -34,7 +34,7 @@ Layout workspace_layout(int B, int n_pred, int V, int top_k) {
     const size_t win = align_up((size_t)n_pred * (size_t)B * 8u);
     l.partials_off = l.winners_off + win;
     const size_t part =
-        top_k > 1 ? align_up((size_t)n_pred * B * (size_t)chain_workgroups(V) * top_k * 8u) : 0;
+        top_k > 1 ? align_up((size_t)n_pred * B * (size_t)chain_workgroups_max(V) * top_k * 8u) : 0;
     l.total = l.partials_off + part;
     return l;
 }
@@ -96,7 +96,7 @@ int run_chain(const float* logits, const void* hidden, int hidden_dtype, const u
     c.r = r;
     c.n_pred = n_pred;
     c.top_k = top_k;
-    c.nwg = chain_workgroups(V);
+    c.nwg = chain_workgroups(B, V, r);
 
     hipError_t e = launch_chain_init(c, stream);
     for (int j = 0; j < n_pred && e == hipSuccess; ++j) e = launch_chain_step(c, j, stream);

@@ -21,15 +21,25 @@ hipError_t launch_lmhead_gemm(const GemmArgs& a, bool hidden_f32, hipStream_t st
 // ---- Markov chain -----------------------------------------------------------
 // Chain step geometry. With V % 4 == 0 the pipelined kernel runs at most
 // kChainMaxWGs workgroups (one per CU), each streaming a contiguous range of
-// kChainTile-column tiles; otherwise the direct kernel runs one workgroup per
-// kChainTileV columns.
-constexpr int kChainTile = 64;
+// tiles of chain_tile(B, r) columns; otherwise the direct kernel runs one
+// workgroup per kChainTileV columns.
 constexpr int kChainMaxWGs = 256;
 constexpr int kChainTileV = 128;
 inline bool chain_pipelined(int V) { return (V & 3) == 0; }
-inline int chain_workgroups(int V) {
+inline int chain_tile(int B, int r) { return (B <= 32 && r <= 128) ? 128 : 64; }
+inline int chain_workgroups(int B, int V, int r) {
     if (chain_pipelined(V)) {
-        const int nt = (V + kChainTile - 1) / kChainTile;
+        const int ts = chain_tile(B, r);
+        const int nt = (V + ts - 1) / ts;
+        return nt < kChainMaxWGs ? nt : kChainMaxWGs;
+    }
+    return (V + kChainTileV - 1) / kChainTileV;
+}
+// Upper bound of chain_workgroups over every rank (workspace sizing does not
+// know r): the narrowest tile gives the most workgroups.
+inline int chain_workgroups_max(int V) {
+    if (chain_pipelined(V)) {
+        const int nt = (V + 63) / 64;
         return nt < kChainMaxWGs ? nt : kChainMaxWGs;
     }
     return (V + kChainTileV - 1) / kChainTileV;

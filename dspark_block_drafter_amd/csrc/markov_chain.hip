@@ -132,15 +132,17 @@ __device__ __forceinline__ int swz_rows(int row) {
     else return 0;
 }
 
-// Workgroup g streams the vocabulary range of tiles [t0, t1) (kChainTile
+// Workgroup g streams the vocabulary range of tiles [t0, t1) (TS = 32 VW
 // columns each) for up to 64 blocks. Every tile's markov_w2 rows and slot-j
 // logits go through an NS-deep ring of LDS stages filled by direct-to-LDS
 // loads, so NS - 1 tiles are in flight while one is scored. Wave w scores the
-// 32 columns (w % 2) of the tile for block group w / 2. The workgroup
-// publishes once per slot, after its whole range.
-template <int NB, int KL, int RS, int NS>
+// 32-column block w % VW of the tile for block group w / VW (VW = 4 when one
+// group of 32 blocks suffices, else 2). The workgroup publishes once per
+// slot, after its whole range.
+template <int NB, int KL, int RS, int NS, int VW>
 __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
-    constexpr int TS = kChainTile;          // columns per tile (two 32-column MFMA blocks)
+    constexpr int TS = 32 * VW;             // columns per tile
+    static_assert(VW * NB <= kWaves && (VW == 2 || VW == 4), "wave split");
     constexpr int WR = 2 * RS;              // 16-byte chunks per staged markov_w2 row
     constexpr int WRd = WR > 0 ? WR : 1;    // (divisor; only used when RS > 0)
     constexpr int LR = TS / 4;              // 16-byte chunks per staged logits row
@@ -149,18 +151,18 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
     constexpr int STAGE = W_SLOTS + L_SLOTS;
     constexpr int W_INST = W_SLOTS / 64, L_INST = L_SLOTS / 64;
     constexpr int LW = (W_INST + L_INST) / kWaves;  // loads per wave per tile
-    static_assert(TS == 64 && (W_INST + L_INST) % kWaves == 0, "tile loads must split over waves");
+    static_assert((W_INST + L_INST) % kWaves == 0, "tile loads must split over waves");
     static_assert(NS >= 2 && (NS - 2) * LW < 64, "pipeline depth");
     static_assert(kWaves * KL * NB * 32 * 8 <= NS * STAGE * 16, "list merge reuses the ring");
     __shared__ u32x4 ring[NS][STAGE];
     // Last-entry score of each wave's lists, per block: a lower bound of the
-    // block's KL-th best score in this workgroup, shared with the wave that
-    // scores the other 32 columns of the same blocks.
+    // block's KL-th best score in this workgroup, shared with the waves that
+    // score the other columns of the same blocks.
     __shared__ float s_thr[kWaves][32];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lrow = lane & 31, lhalf = lane >> 5;
-    const int vb = wave & 1, nbw = wave >> 1;        // this wave's 32-column block / block group
+    const int vb = wave % VW, nbw = wave / VW;       // this wave's 32-column block / block group
     const int bbase = blockIdx.y * NB * 32;
     const int B = a.B, V = a.V, r = a.r;
     const int nT = (V + TS - 1) / TS, G = gridDim.x, g = blockIdx.x;
@@ -296,7 +298,8 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
                 // Hits are inserted in rounds, one per lane per round.
                 float thr = list[KL - 1] != 0ull ? key_score(list[KL - 1]) : -INFINITY;
                 thr = fmaxf(thr, __shfl_xor(thr, 32, kWave));
-                thr = fmaxf(thr, s_thr[wave ^ 1][lrow]);
+#pragma unroll
+                for (int w = 0; w < VW; ++w) thr = fmaxf(thr, s_thr[nbw * VW + w][lrow]);
                 unsigned hits = 0u;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) hits |= (z[e] > thr ? 1u : 0u) << e;
@@ -333,7 +336,7 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
         st = st + 1 == NS ? 0 : st + 1;
     }
 
-    // Merge: the lane pair that holds the same block, then the two waves of
+    // Merge: the lane pair that holds the same block, then the VW waves of
     // the block group (their lists go through the ring, free by now).
     {
         u64 other[KL];
@@ -351,7 +354,9 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
     __syncthreads();
     if (vb == 0 && lhalf == 0 && active) {
 #pragma unroll
-        for (int i = 0; i < KL; ++i) topk_insert<KL>(list, s_list[((wave + 1) * 32 + lrow) * KL + i]);
+        for (int w = 1; w < VW; ++w)
+#pragma unroll
+            for (int i = 0; i < KL; ++i) topk_insert<KL>(list, s_list[((wave + w) * 32 + lrow) * KL + i]);
         const int b = bme;
         if (a.top_k > 1) {
             u64* p = a.partials + (((long)j * B + b) * a.nwg + g) * a.top_k;
@@ -539,12 +544,22 @@ hipError_t step_direct(const ChainArgs& a, int j, dim3 grid, hipStream_t s) {
 template <int NB, int KL>
 hipError_t step_pipe(const ChainArgs& a, int j, dim3 grid, hipStream_t s) {
     const int rs = (a.r + 15) / 16;
-#define DSPARK_STEP(RSV, NSV) hipLaunchKernelGGL((chain_step_pipe<NB, KL, RSV, NSV>), grid, dim3(256), 0, s, a, j);
-    if (rs == 0) { DSPARK_STEP(0, 4) }
-    else if (rs <= 2) { DSPARK_STEP(2, 4) }
-    else if (rs <= 4) { DSPARK_STEP(4, 4) }
-    else if (rs <= 8) { DSPARK_STEP(8, 4) }
-    else { DSPARK_STEP(16, 3) }
+#define DSPARK_STEP(RSV, NSV, VWV) \
+    hipLaunchKernelGGL((chain_step_pipe<NB, KL, RSV, NSV, VWV>), grid, dim3(256), 0, s, a, j);
+    if constexpr (NB == 1) {
+        // one block group: all four waves take their own 32 columns
+        if (rs == 0) { DSPARK_STEP(0, 4, 4) }
+        else if (rs <= 2) { DSPARK_STEP(2, 4, 4) }
+        else if (rs <= 4) { DSPARK_STEP(4, 4, 4) }
+        else if (rs <= 8) { DSPARK_STEP(8, 3, 4) }
+        else { DSPARK_STEP(16, 3, 2) }
+    } else {
+        if (rs == 0) { DSPARK_STEP(0, 4, 2) }
+        else if (rs <= 2) { DSPARK_STEP(2, 4, 2) }
+        else if (rs <= 4) { DSPARK_STEP(4, 4, 2) }
+        else if (rs <= 8) { DSPARK_STEP(8, 4, 2) }
+        else { DSPARK_STEP(16, 3, 2) }
+    }
 #undef DSPARK_STEP
     return hipGetLastError();
 }
