@@ -196,6 +196,13 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
     // last 16-byte chunk of the row; such columns are never scored.
     auto issue = [&](int st, int t) {
         const int v0 = t * TS;
+        if (v0 + TS <= V) {   // whole tile inside the vocabulary: no clamping
+#pragma unroll
+            for (int i = 0; i < LW; ++i)
+                __builtin_amdgcn_global_load_lds((const void*)(src[i] + (long)t * step[i]),
+                                                 (lds_ptr)&ring[st][dst[i]], 16, 0, 0);
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < LW; ++i) {
             const char* p = src[i] + (long)t * step[i];
@@ -259,24 +266,29 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
         if (wave_on) {
             const u32x4* stg = ring[st];
             const int vrow = vb * 32 + lrow;
-            f32x16 acc = f32x16{};
-#pragma unroll
-            for (int s = 0; s < RS; ++s) {
-                const u32x4 w = stg[vrow * WR + ((2 * s + lhalf) ^ swz_rows<WR>(vrow))];
-                acc = mfma32x32x16(w, u[s], acc);
-            }
             const int row = nbw * 32 + lrow;
             const int vt = (t0 + it) * TS + vb * 32;
-            // z[4q + e] is the biased score of column vt + 8q + 4(lane/32) + e.
-            float z[16];
+            // logits reads first (their latency hides behind the MFMAs), then
+            // the bias product as two independent accumulation chains
+            f32x4 x[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int c = vb * 8 + 2 * q + lhalf;
-                const f32x4 x = __builtin_bit_cast(
-                    f32x4, stg[W_SLOTS + row * LR + (c ^ swz_rows<LR>(row))]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) z[4 * q + e] = x[e] + acc[4 * q + e];
+                x[q] = __builtin_bit_cast(f32x4, stg[W_SLOTS + row * LR + (c ^ swz_rows<LR>(row))]);
             }
+            f32x16 acc0 = f32x16{}, acc1 = f32x16{};
+#pragma unroll
+            for (int s = 0; s < RS; ++s) {
+                const u32x4 w = stg[vrow * WR + ((2 * s + lhalf) ^ swz_rows<WR>(vrow))];
+                if (s & 1) acc1 = mfma32x32x16(w, u[s], acc1);
+                else acc0 = mfma32x32x16(w, u[s], acc0);
+            }
+            // z[4q + e] is the biased score of column vt + 8q + 4(lane/32) + e.
+            float z[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) z[4 * q + e] = x[q][e] + (acc0[4 * q + e] + acc1[4 * q + e]);
             const int vlane = vt + 4 * lhalf;
             const bool full = vt + 32 <= V;
             if (KL == 1 || it == 0 || !full) {
