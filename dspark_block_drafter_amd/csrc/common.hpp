@@ -111,6 +111,11 @@ __device__ __forceinline__ void wait_stages(int newer) {
     }
 }
 
+// Wait until every LDS read this wave issued has returned its data.
+__device__ __forceinline__ void wait_lds_reads() {
+    __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
+}
+
 __device__ __forceinline__ void block_barrier() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();

@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
     constexpr int W_INST = W_SLOTS / 64, L_INST = L_SLOTS / 64;
     constexpr int LW = (W_INST + L_INST) / kWaves;  // loads per wave per tile
     static_assert((W_INST + L_INST) % kWaves == 0, "tile loads must split over waves");
-    static_assert(NS >= 2 && (NS - 2) * LW < 64, "pipeline depth");
+    static_assert(NS >= 2 && (NS - 1) * LW < 64, "pipeline depth");
     static_assert(kWaves * KL * NB * 32 * 8 <= NS * STAGE * 16, "list merge reuses the ring");
     __shared__ u32x4 ring[NS][STAGE];
     // Last-entry score of each wave's lists, per block: a lower bound of the
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
     }
     // Columns past V: markov_w2 rows are clamped to row V-1, logits to the
     // last 16-byte chunk of the row; such columns are never scored.
-    auto issue = [&](int st, int t) {
+    auto issue = [&](int st, int t) __attribute__((always_inline)) {
         const int v0 = t * TS;
         if (v0 + TS <= V) {   // whole tile inside the vocabulary: no clamping
 #pragma unroll
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
     // for ring stages (a register load still in flight there would make every
     // iteration drain the whole ring).
 #pragma unroll
-    for (int t = 0; t < NS - 2; ++t)
+    for (int t = 0; t < NS - 1; ++t)
         if (t < n) issue(t, t0 + t);
     u32x4 u[RS > 0 ? RS : 1];
 #pragma unroll
@@ -255,97 +255,120 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
     for (int i = 0; i < KL; ++i) list[i] = 0ull;
     if (lhalf == 0) s_thr[wave][lrow] = -INFINITY;
 
-    int st = 0;
-    for (int it = 0; it < n; ++it) {
-        // Tile it + NS - 2 goes into the stage of tile it - 2, which every wave
-        // finished before passing the previous barrier; issuing it before this
-        // iteration's wait keeps the ring full while slow waves catch up.
-        if (it + NS - 2 < n) issue((st + NS - 2) % NS, t0 + it + NS - 2);
-        wait_stages<LW, NS - 2>(min(NS - 2, n - 1 - it));
-        block_barrier();
-        if (wave_on) {
-            const u32x4* stg = ring[st];
-            const int vrow = vb * 32 + lrow;
-            const int row = nbw * 32 + lrow;
-            const int vt = (t0 + it) * TS + vb * 32;
-            // logits reads first (their latency hides behind the MFMAs), then
-            // the bias product as two independent accumulation chains
-            f32x4 x[4];
+    // Software pipeline over tiles: the bias product of tile it + 1 (LDS
+    // reads + MFMA) is issued before the top-k work of tile it, so the matrix
+    // pipe runs while the wave inserts. Tile it + NS - 1 is loaded into the
+    // stage of tile it - 1, which every wave finished reading (score of tile
+    // it - 1, one iteration earlier) before it passed the previous barrier.
+    struct Scores { f32x4 x[4]; f32x16 a0, a1; };
+    auto score = [&](int st_, Scores& sc) __attribute__((always_inline)) {
+        const u32x4* stg = ring[st_];
+        const int vrow = vb * 32 + lrow;
+        const int row = nbw * 32 + lrow;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int c = vb * 8 + 2 * q + lhalf;
-                x[q] = __builtin_bit_cast(f32x4, stg[W_SLOTS + row * LR + (c ^ swz_rows<LR>(row))]);
-            }
-            f32x16 acc0 = f32x16{}, acc1 = f32x16{};
+        for (int q = 0; q < 4; ++q) {
+            const int c = vb * 8 + 2 * q + lhalf;
+            sc.x[q] = __builtin_bit_cast(f32x4, stg[W_SLOTS + row * LR + (c ^ swz_rows<LR>(row))]);
+        }
+        sc.a0 = f32x16{};
+        sc.a1 = f32x16{};
 #pragma unroll
-            for (int s = 0; s < RS; ++s) {
-                const u32x4 w = stg[vrow * WR + ((2 * s + lhalf) ^ swz_rows<WR>(vrow))];
-                if (s & 1) acc1 = mfma32x32x16(w, u[s], acc1);
-                else acc0 = mfma32x32x16(w, u[s], acc0);
-            }
-            // z[4q + e] is the biased score of column vt + 8q + 4(lane/32) + e.
-            float z[16];
+        for (int s = 0; s < RS; ++s) {
+            const u32x4 w = stg[vrow * WR + ((2 * s + lhalf) ^ swz_rows<WR>(vrow))];
+            if (s & 1) sc.a1 = mfma32x32x16(w, u[s], sc.a1);
+            else sc.a0 = mfma32x32x16(w, u[s], sc.a0);
+        }
+    };
+    auto consume = [&](int it, const Scores& sc) __attribute__((always_inline)) {
+        const int vt = (t0 + it) * TS + vb * 32;
+        // z[4q + e] is the biased score of column vt + 8q + 4(lane/32) + e.
+        float z[16];
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) z[4 * q + e] = x[q][e] + (acc0[4 * q + e] + acc1[4 * q + e]);
-            const int vlane = vt + 4 * lhalf;
-            const bool full = vt + 32 <= V;
-            if (KL == 1 || it == 0 || !full) {
-                // plain inserts (argmax lists, the first tile, the ragged last tile)
+            for (int e = 0; e < 4; ++e) z[4 * q + e] = sc.x[q][e] + (sc.a0[4 * q + e] + sc.a1[4 * q + e]);
+        const int vlane = vt + 4 * lhalf;
+        const bool full = vt + 32 <= V;
+        if (KL == 1 || it == 0 || !full) {
+            // plain inserts (argmax lists, the first tile, the ragged last tile)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int v = vlane + 8 * (e >> 2) + (e & 3);
-                    if (active && v < V) {
-                        const u64 key = make_key(z[e], v);
-                        if (key > list[KL - 1]) topk_insert<KL>(list, key);
-                    }
-                }
-            } else {
-                // Filtered inserts: a score can only enter this lane's list if it
-                // beats the list's last entry, and cannot be among the block's
-                // best KL if it does not beat the last entry of the partner
-                // lane's list either (both lists are subsets of the block's
-                // scores; a lane's ids rise, so ties go to the listed entry).
-                // Hits are inserted in rounds, one per lane per round.
-                float thr = list[KL - 1] != 0ull ? key_score(list[KL - 1]) : -INFINITY;
-                thr = fmaxf(thr, __shfl_xor(thr, 32, kWave));
-#pragma unroll
-                for (int w = 0; w < VW; ++w) thr = fmaxf(thr, s_thr[nbw * VW + w][lrow]);
-                unsigned hits = 0u;
-#pragma unroll
-                for (int e = 0; e < 16; ++e) hits |= (z[e] > thr ? 1u : 0u) << e;
-                if (!active) hits = 0u;
-                while (__any(hits != 0u)) {
-                    if (hits != 0u) {
-                        const int e = __builtin_ctz(hits);
-                        hits &= hits - 1u;
-                        // z[e] by a select tree on the bits of e
-                        const u64 m0 = __builtin_amdgcn_ballot_w64((e & 1) != 0);
-                        const u64 m1 = __builtin_amdgcn_ballot_w64((e & 2) != 0);
-                        const u64 m2 = __builtin_amdgcn_ballot_w64((e & 4) != 0);
-                        const u64 m3 = __builtin_amdgcn_ballot_w64((e & 8) != 0);
-                        float s8[8], s4[4], s2[2];
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) s8[i] = lane_select(z[2 * i + 1], z[2 * i], m0);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) s4[i] = lane_select(s8[2 * i + 1], s8[2 * i], m1);
-#pragma unroll
-                        for (int i = 0; i < 2; ++i) s2[i] = lane_select(s4[2 * i + 1], s4[2 * i], m2);
-                        const float ze = lane_select(s2[1], s2[0], m3);
-                        const u64 key = make_key(ze, vlane + 8 * (e >> 2) + (e & 3));
-                        if (key > list[KL - 1]) topk_insert<KL>(list, key);
-                    }
+            for (int e = 0; e < 16; ++e) {
+                const int v = vlane + 8 * (e >> 2) + (e & 3);
+                if (active && v < V) {
+                    const u64 key = make_key(z[e], v);
+                    if (key > list[KL - 1]) topk_insert<KL>(list, key);
                 }
             }
-            if (KL > 1) {
-                // publish this wave's bound for the partner wave's next tile
-                float own = list[KL - 1] != 0ull ? key_score(list[KL - 1]) : -INFINITY;
-                own = fmaxf(own, __shfl_xor(own, 32, kWave));
-                if (lhalf == 0) s_thr[wave][lrow] = own;
+        } else {
+            // Filtered inserts: a score can only enter this lane's list if it
+            // beats the list's last entry, and cannot be among the block's
+            // best KL if it does not beat the last entry of the partner
+            // lane's list either (both lists are subsets of the block's
+            // scores; a lane's ids rise, so ties go to the listed entry).
+            // Hits are inserted in rounds, one per lane per round.
+            float thr = list[KL - 1] != 0ull ? key_score(list[KL - 1]) : -INFINITY;
+            thr = fmaxf(thr, __shfl_xor(thr, 32, kWave));
+#pragma unroll
+            for (int w = 0; w < VW; ++w) thr = fmaxf(thr, s_thr[nbw * VW + w][lrow]);
+            unsigned hits = 0u;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) hits |= (z[e] > thr ? 1u : 0u) << e;
+            if (!active) hits = 0u;
+            while (__any(hits != 0u)) {
+                if (hits != 0u) {
+                    const int e = __builtin_ctz(hits);
+                    hits &= hits - 1u;
+                    // z[e] by a select tree on the bits of e
+                    const u64 m0 = __builtin_amdgcn_ballot_w64((e & 1) != 0);
+                    const u64 m1 = __builtin_amdgcn_ballot_w64((e & 2) != 0);
+                    const u64 m2 = __builtin_amdgcn_ballot_w64((e & 4) != 0);
+                    const u64 m3 = __builtin_amdgcn_ballot_w64((e & 8) != 0);
+                    float s8[8], s4[4], s2[2];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) s8[i] = lane_select(z[2 * i + 1], z[2 * i], m0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) s4[i] = lane_select(s8[2 * i + 1], s8[2 * i], m1);
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) s2[i] = lane_select(s4[2 * i + 1], s4[2 * i], m2);
+                    const float ze = lane_select(s2[1], s2[0], m3);
+                    const u64 key = make_key(ze, vlane + 8 * (e >> 2) + (e & 3));
+                    if (key > list[KL - 1]) topk_insert<KL>(list, key);
+                }
             }
         }
-        st = st + 1 == NS ? 0 : st + 1;
+        if (KL > 1) {
+            // publish this wave's bound for the partner wave's next tile
+            float own = list[KL - 1] != 0ull ? key_score(list[KL - 1]) : -INFINITY;
+            own = fmaxf(own, __shfl_xor(own, 32, kWave));
+            if (lhalf == 0) s_thr[wave][lrow] = own;
+        }
+    };
+    // one iteration: bring tile it + 1 in and score it, then consume tile it
+    auto step_tile = [&](int it, int& st, const Scores& cur, Scores& nxt) __attribute__((always_inline)) {
+        const int nst = st + 1 == NS ? 0 : st + 1;
+        if (it + 1 < n) {
+            if (it + NS - 1 < n) issue((st + NS - 1) % NS, t0 + it + NS - 1);
+            wait_stages<LW, NS - 2>(min(NS - 2, n - 2 - it));
+            // The logits of tile it were read into registers before this
+            // barrier; their reads must have landed before any wave refills
+            // that stage after it.
+            wait_lds_reads();
+            block_barrier();
+            if (wave_on) score(nst, nxt);
+        }
+        if (wave_on) consume(it, cur);
+        st = nst;
+    };
+
+    // Tiles 0 .. NS - 2 have landed (the full wait above); stage NS - 1 is
+    // filled by the first iteration.
+    int st = 0;
+    Scores S0, S1;
+    block_barrier();
+    if (n > 0 && wave_on) score(0, S0);
+    for (int it = 0; it < n; it += 2) {
+        step_tile(it, st, S0, S1);
+        if (it + 1 < n) step_tile(it + 1, st, S1, S0);
     }
 
     // Merge: the lane pair that holds the same block, then the VW waves of
