@@ -260,7 +260,9 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
     // pipe runs while the wave inserts. Tile it + NS - 1 is loaded into the
     // stage of tile it - 1, which every wave finished reading (score of tile
     // it - 1, one iteration earlier) before it passed the previous barrier.
-    struct Scores { f32x4 x[4]; f32x16 a0, a1; };
+    // The slot-j logits of a tile enter the MFMA as its accumulator input, so
+    // the accumulator ends as the biased score z = logits + W2 . W1[prev].
+    struct Scores { f32x16 acc; };
     auto score = [&](int st_, Scores& sc) __attribute__((always_inline)) {
         const u32x4* stg = ring[st_];
         const int vrow = vb * 32 + lrow;
@@ -268,29 +270,27 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int c = vb * 8 + 2 * q + lhalf;
-            sc.x[q] = __builtin_bit_cast(f32x4, stg[W_SLOTS + row * LR + (c ^ swz_rows<LR>(row))]);
+            const f32x4 x = __builtin_bit_cast(f32x4, stg[W_SLOTS + row * LR + (c ^ swz_rows<LR>(row))]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sc.acc[4 * q + e] = x[e];
         }
-        sc.a0 = f32x16{};
-        sc.a1 = f32x16{};
 #pragma unroll
         for (int s = 0; s < RS; ++s) {
             const u32x4 w = stg[vrow * WR + ((2 * s + lhalf) ^ swz_rows<WR>(vrow))];
-            if (s & 1) sc.a1 = mfma32x32x16(w, u[s], sc.a1);
-            else sc.a0 = mfma32x32x16(w, u[s], sc.a0);
+            sc.acc = mfma32x32x16(w, u[s], sc.acc);
         }
     };
     auto consume = [&](int it, const Scores& sc) __attribute__((always_inline)) {
         const int vt = (t0 + it) * TS + vb * 32;
-        // z[4q + e] is the biased score of column vt + 8q + 4(lane/32) + e.
+        // z[4q + e] is the biased score of column vt + 8q + 4(lane/32) + e;
+        // the column rises with the index.
         float z[16];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) z[4 * q + e] = sc.x[q][e] + (sc.a0[4 * q + e] + sc.a1[4 * q + e]);
+        for (int e = 0; e < 16; ++e) z[e] = sc.acc[e];
         const int vlane = vt + 4 * lhalf;
         const bool full = vt + 32 <= V;
-        if (KL == 1 || it == 0 || !full) {
-            // plain inserts (argmax lists, the first tile, the ragged last tile)
+        if (!full || (KL > 1 && it == 0)) {
+            // plain inserts (the ragged last tile; the first tile of top-k lists)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int v = vlane + 8 * (e >> 2) + (e & 3);
@@ -299,40 +299,60 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
                     if (key > list[KL - 1]) topk_insert<KL>(list, key);
                 }
             }
+        } else if constexpr (KL == 1) {
+            // Argmax of the lane's 16 columns: a strictly greater score moves
+            // the pick, so equal scores keep the lower column, as the key
+            // order does.
+            float best = z[0];
+            int be = 0;
+#pragma unroll
+            for (int e = 1; e < 16; ++e) {
+                const bool gt = z[e] > best;
+                best = gt ? z[e] : best;
+                be = gt ? e : be;
+            }
+            const u64 key = make_key(best, vlane + 8 * (be >> 2) + (be & 3));
+            if (active && key > list[0]) list[0] = key;
         } else {
             // Filtered inserts: a score can only enter this lane's list if it
-            // beats the list's last entry, and cannot be among the block's
-            // best KL if it does not beat the last entry of the partner
-            // lane's list either (both lists are subsets of the block's
-            // scores; a lane's ids rise, so ties go to the listed entry).
-            // Hits are inserted in rounds, one per lane per round.
+            // reaches the list's last entry, and cannot be among the block's
+            // best KL if it is below the last entry of the partner lane's
+            // list or of the other waves' lists for the same blocks (every
+            // such list holds KL scores of the block). A score equal to the
+            // bound passes, so the full key comparison settles ties by
+            // column. Hits are inserted in rounds, one per lane per round.
             float thr = list[KL - 1] != 0ull ? key_score(list[KL - 1]) : -INFINITY;
             thr = fmaxf(thr, __shfl_xor(thr, 32, kWave));
 #pragma unroll
             for (int w = 0; w < VW; ++w) thr = fmaxf(thr, s_thr[nbw * VW + w][lrow]);
-            unsigned hits = 0u;
+            float zmax = z[0];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) hits |= (z[e] > thr ? 1u : 0u) << e;
-            if (!active) hits = 0u;
-            while (__any(hits != 0u)) {
-                if (hits != 0u) {
-                    const int e = __builtin_ctz(hits);
-                    hits &= hits - 1u;
-                    // z[e] by a select tree on the bits of e
-                    const u64 m0 = __builtin_amdgcn_ballot_w64((e & 1) != 0);
-                    const u64 m1 = __builtin_amdgcn_ballot_w64((e & 2) != 0);
-                    const u64 m2 = __builtin_amdgcn_ballot_w64((e & 4) != 0);
-                    const u64 m3 = __builtin_amdgcn_ballot_w64((e & 8) != 0);
-                    float s8[8], s4[4], s2[2];
+            for (int e = 1; e < 16; ++e) zmax = fmaxf(zmax, z[e]);
+            if (__any(active && zmax >= thr)) {
+                unsigned hits = 0u;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) s8[i] = lane_select(z[2 * i + 1], z[2 * i], m0);
+                for (int e = 0; e < 16; ++e) hits |= (z[e] >= thr ? 1u : 0u) << e;
+                if (!active) hits = 0u;
+                while (__any(hits != 0u)) {
+                    if (hits != 0u) {
+                        const int e = __builtin_ctz(hits);
+                        hits &= hits - 1u;
+                        // z[e] by a select tree on the bits of e
+                        const u64 m0 = __builtin_amdgcn_ballot_w64((e & 1) != 0);
+                        const u64 m1 = __builtin_amdgcn_ballot_w64((e & 2) != 0);
+                        const u64 m2 = __builtin_amdgcn_ballot_w64((e & 4) != 0);
+                        const u64 m3 = __builtin_amdgcn_ballot_w64((e & 8) != 0);
+                        float s8[8], s4[4], s2[2];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) s4[i] = lane_select(s8[2 * i + 1], s8[2 * i], m1);
+                        for (int i = 0; i < 8; ++i) s8[i] = lane_select(z[2 * i + 1], z[2 * i], m0);
 #pragma unroll
-                    for (int i = 0; i < 2; ++i) s2[i] = lane_select(s4[2 * i + 1], s4[2 * i], m2);
-                    const float ze = lane_select(s2[1], s2[0], m3);
-                    const u64 key = make_key(ze, vlane + 8 * (e >> 2) + (e & 3));
-                    if (key > list[KL - 1]) topk_insert<KL>(list, key);
+                        for (int i = 0; i < 4; ++i) s4[i] = lane_select(s8[2 * i + 1], s8[2 * i], m1);
+#pragma unroll
+                        for (int i = 0; i < 2; ++i) s2[i] = lane_select(s4[2 * i + 1], s4[2 * i], m2);
+                        const float ze = lane_select(s2[1], s2[0], m3);
+                        const u64 key = make_key(ze, vlane + 8 * (e >> 2) + (e & 3));
+                        if (key > list[KL - 1]) topk_insert<KL>(list, key);
+                    }
                 }
             }
         }
