@@ -328,16 +328,23 @@ __global__ __launch_bounds__(64 * WM * WN) void lmhead_gemm_dma(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Split-ring pipeline for large M (bf16 hidden, K % 64 == 0).
+// Four-wave pipeline for large M (bf16 hidden, K % 64 == 0).
 //
-// K advances 64 at a time: a stage row is one 128-byte line. The two operands
-// get rings sized to their latency: the hidden rows (A) are re-read by every
-// lm_head slab and stay in L2, so two stages suffice; the lm_head rows (B) are
-// read from HBM once, so they get three stages and two of them are always in
-// flight. Per iteration the loads are issued A(kt+1) first, then
-// B(kt+NSB-1), so that the in-order vmcnt wait for A(kt) never has to wait
-// for the newest B loads. Both rings live in one LDS array: with separate
-// arrays the compiler drains every in-flight LDS load before each LDS read.
+// A 256 x 256 tile per workgroup of four waves; each wave owns a 128 x 128
+// quarter (4 x 4 MFMA blocks, all 256 accumulator registers), which needs
+// 8 operand reads from LDS per 16 MFMAs. K advances 64 at a time (a stage row
+// is one 128-byte line, chunks swizzled as above). The hidden rows (A) are
+// re-read by every lm_head slab and stay in L2, so their ring has two stages;
+// the lm_head rows (B) come from HBM once and get three. Loads go straight
+// into LDS through buffer loads (the per-lane state is a 32-bit offset; the
+// lm_head descriptor covers exactly this tile's rows, so rows past N read as
+// zero). One barrier per K step, at its start. The step is cut into four
+// regions of 16 products; every region carries the LDS reads of the next
+// k-substep and the first one also the global->LDS loads of later stages, each
+// interleaved between the products (sched_group_barrier), so the matrix pipe
+// is never left waiting on an issue burst. Past the last K step the loads
+// repeat the last step into stages that are not read again, which keeps the
+// step free of branches.
 // ---------------------------------------------------------------------------
 template <int CH>
 __device__ __forceinline__ int swz_ch(int row) {
@@ -345,60 +352,55 @@ __device__ __forceinline__ int swz_ch(int row) {
     else return swz(row);
 }
 
-template <int BM, int BN, int WM, int WN, int NSA, int NSB>
-__global__ __launch_bounds__(64 * WM * WN) void lmhead_gemm_split(GemmArgs a) {
-    constexpr int NW = WM * WN;
-    constexpr int TM = BM / WM, TN = BN / WN;
-    constexpr int FM = TM / 32, FN = TN / 32;
-    constexpr int BKS = 64, CH = BKS / 8;
-    constexpr int IA = BM * CH / 64, IB = BN * CH / 64;  // 1 KB wave-loads per stage
-    constexpr int LA = IA / NW, LB = IB / NW;
-    static_assert(IA % NW == 0 && IB % NW == 0, "stage loads must split evenly over waves");
-    static_assert(NSA == 2 && NSB >= 2, "ring depths");
-    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
-    constexpr int BOFF = NSA * BM * CH;
-    __shared__ u32x4 smem[NSA * BM * CH + NSB * BN * CH];
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, unsigned bytes) {
+    // raw buffer (stride 0): accesses at or past `bytes` read as zero
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+__global__ __launch_bounds__(256) void lmhead_gemm_w4(GemmArgs a) {
+    constexpr int BM = 256, BN = 256, BKS = 64, CH = 8, FM = 4, FN = 4, NSA = 2, NSB = 3;
+    constexpr int ASTG = BM * CH * 16, BSTG = BN * CH * 16;   // bytes per stage
+    constexpr int LA = 8, LB = 8;                              // 1 KB loads per wave per stage
+    __shared__ __attribute__((aligned(1024))) char smem[NSA * ASTG + NSB * BSTG];
 
     const int M = a.M, N = a.N, K = a.K;
     const int nMT = (M + BM - 1) / BM, nNT = (N + BN - 1) / BN, T = nMT * nNT;
     const int bid = blockIdx.x;
     const int sid = (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
     const int m0 = (sid % nMT) * BM, n0 = (sid / nMT) * BN;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WN, wn = wave % WN;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
 
-    // The lane that owns LDS slot p of a stage fetches the chunk the swizzle
-    // puts there; rows past M / N are clamped (their products are not stored).
-    const uint16_t* srcA[LA];
-    const uint16_t* srcB[LB];
-    int dstA[LA], dstB[LB];
+    // Load i of this wave fills LDS slots (wave + 4 i) * 64 + lane of a stage:
+    // row 32 i + 8 wave + lane / 8, position lane % 8, which holds the chunk
+    // the swizzle puts there.
+    const rsrc_t ra = make_rsrc(a.hidden, 0xFFFFFFFFu);
+    const rsrc_t rb = make_rsrc(a.lm_head + (long)n0 * K, (unsigned)min(BN, N - n0) * K * 2);
+    const int p = lane & 7, r8 = lane >> 3;
+    unsigned aoff[LA];
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
-        const int inst = wave + i * NW, slot = inst * 64 + lane;
-        const int row = slot / CH, c = (slot % CH) ^ swz_ch<CH>(row);
+        const int row = 32 * i + 8 * wave + r8;
         const int m = min(m0 + row, M - 1);
         const long hrow = (long)(m / a.n_pred) * a.L + a.i_first + m % a.n_pred;
-        srcA[i] = static_cast<const uint16_t*>(a.hidden) + hrow * K + c * 8;
-        dstA[i] = inst * 64;
+        aoff[i] = (unsigned)(hrow * K * 2 + (p ^ swz_ch<CH>(row)) * 16);
     }
+    // lm_head rows are linear in i; the swizzle depends on i only by parity
+    unsigned boff[2];
 #pragma unroll
-    for (int i = 0; i < LB; ++i) {
-        const int inst = wave + i * NW, slot = inst * 64 + lane;
-        const int row = slot / CH, c = (slot % CH) ^ swz_ch<CH>(row);
-        srcB[i] = a.lm_head + (long)min(n0 + row, N - 1) * K + c * 8;
-        dstB[i] = inst * 64;
+    for (int q = 0; q < 2; ++q) {
+        const int row = 32 * q + 8 * wave + r8;
+        boff[q] = (unsigned)((8 * wave + r8) * K * 2 + (p ^ swz_ch<CH>(row)) * 16);
     }
-    auto issueA = [&](int st, int k0) {
-#pragma unroll
-        for (int i = 0; i < LA; ++i)
-            __builtin_amdgcn_global_load_lds((const void*)(srcA[i] + k0),
-                                             (lds_ptr)&smem[st * BM * CH + dstA[i]], 16, 0, 0);
+    auto loadA = [&](int st, int kb, int i) __attribute__((always_inline)) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(smem + st * ASTG + (wave + 4 * i) * 1024), 16,
+                                                 aoff[i], kb, 0, 0);
     };
-    auto issueB = [&](int st, int k0) {
-#pragma unroll
-        for (int i = 0; i < LB; ++i)
-            __builtin_amdgcn_global_load_lds((const void*)(srcB[i] + k0),
-                                             (lds_ptr)&smem[BOFF + st * BN * CH + dstB[i]], 16, 0, 0);
+    auto loadB = [&](int st, int kb, int i) __attribute__((always_inline)) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr)(smem + NSA * ASTG + st * BSTG + (wave + 4 * i) * 1024),
+                                                 16, boff[i & 1], i * 32 * K * 2 + kb, 0, 0);
     };
 
     f32x16 acc[FM][FN];
@@ -406,51 +408,108 @@ __global__ __launch_bounds__(64 * WM * WN) void lmhead_gemm_split(GemmArgs a) {
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+    // Fragment i of A: rows wm*128 + 32 i + lrow (B likewise with wn); the
+    // swizzle depends on i only by parity.
     const int lrow = lane & 31, lhalf = lane >> 5;
-    auto mma = [&](int stA, int stB) {
+    int fa_base[2], fb_base[2];
 #pragma unroll
-        for (int ks = 0; ks < BKS / 16; ++ks) {
-            const int ch = ks * 2 + lhalf;
-            u32x4 fa[FM], fb[FN];
+    for (int q = 0; q < 2; ++q) {
+        fa_base[q] = (wm * 128 + lrow) * 128 + (swz_ch<CH>(wm * 128 + 32 * q + lrow) << 4);
+        fb_base[q] = (wn * 128 + lrow) * 128 + (swz_ch<CH>(wn * 128 + 32 * q + lrow) << 4);
+    }
+    auto rdA = [&](int sa, int ks, int i) __attribute__((always_inline)) {
+        const int cx = (2 * ks + lhalf) << 4;
+        return *reinterpret_cast<const u32x4*>(smem + sa * ASTG + i * 4096 + (fa_base[i & 1] ^ cx));
+    };
+    auto rdB = [&](int sb, int ks, int j) __attribute__((always_inline)) {
+        const int cx = (2 * ks + lhalf) << 4;
+        return *reinterpret_cast<const u32x4*>(smem + NSA * ASTG + sb * BSTG + j * 4096 + (fb_base[j & 1] ^ cx));
+    };
+    auto products = [&](const u32x4 (&fa)[FM], const u32x4 (&fb)[FN]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const int row = wm * TM + i * 32 + lrow;
-                fa[i] = smem[stA * BM * CH + row * CH + (ch ^ swz_ch<CH>(row))];
-            }
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int row = wn * TN + j * 32 + lrow;
-                fb[j] = smem[BOFF + stB * BN * CH + row * CH + (ch ^ swz_ch<CH>(row))];
-            }
+            for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16(fa[i], fb[j], acc[i][j]);
+    };
+    // 16 products of (fa, fb) with the reads of k-substep ks into (nfa, nfb)
+    auto region = [&](const u32x4 (&fa)[FM], const u32x4 (&fb)[FN], u32x4 (&nfa)[FM], u32x4 (&nfb)[FN],
+                      int sa, int sb, int ks) __attribute__((always_inline)) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < FM; ++i) nfa[i] = rdA(sa, ks, i);
 #pragma unroll
-                for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16(fa[i], fb[j], acc[i][j]);
+        for (int j = 0; j < FN; ++j) nfb[j] = rdB(sb, ks, j);
+        products(fa, fb);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
         }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     };
 
     const int nK = K / BKS;
-    // Prologue order: B(0 .. NSB-3), A(0), B(NSB-2): at kt = 0 only the newest
-    // B stage may still be in flight.
+    // Prologue: A(0), B(0), B(1). During step t, A(t+1) and then B(t+2) are
+    // issued, so at the start of step t + 1 only B(t+2) may still fly.
 #pragma unroll
-    for (int t = 0; t < NSB - 2; ++t)
-        if (t < nK) issueB(t, t * BKS);
-    issueA(0, 0);
-    if (NSB - 2 < nK) issueB(NSB - 2, (NSB - 2) * BKS);
+    for (int i = 0; i < LA; ++i) loadA(0, 0, i);
+#pragma unroll
+    for (int i = 0; i < LB; ++i) loadB(0, 0, i);
+#pragma unroll
+    for (int i = 0; i < LB; ++i) loadB(1, min(1, nK - 1) * BKS * 2, i);
 
-    int sA = 0, sB = 0;
-    for (int kt = 0; kt < nK; ++kt) {
-        // Loads issued after A(kt): B(kt + NSB - 2) only, when it exists.
-        if (kt + NSB - 2 < nK) wait_vmcnt<LB>();
-        else wait_vmcnt<0>();
-        block_barrier();  // A(kt), B(kt) landed for every wave; stages of kt-1 are free
-        if (kt + 1 < nK) issueA(sA ^ 1, (kt + 1) * BKS);
-        if (kt + NSB - 1 < nK) issueB((sB + NSB - 1) % NSB, (kt + NSB - 1) * BKS);
-        mma(sA, sB);
-        sA ^= 1;
-        sB = sB + 1 == NSB ? 0 : sB + 1;
+    u32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa1[i] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb1[j] = u32x4{0u, 0u, 0u, 0u};
+    int sa = 0, sb = 0;
+    for (int t = 0; t < nK; ++t) {
+        // stage t has landed; every wave has finished reading stage t - 1
+        wait_vmcnt<LB>();
+        block_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        {
+            // k-substep 3 of step t - 1 (zero fragments at t = 0), the reads
+            // of (t, 0), and the loads A(t+1), B(t+2) into the stages of t - 1
+            const int pa = sa ^ 1, pb = sb == 0 ? NSB - 1 : sb - 1;
+            const int kA = min(t + 1, nK - 1) * BKS * 2, kB = min(t + 2, nK - 1) * BKS * 2;
+#pragma unroll
+            for (int i = 0; i < FM; ++i) fa0[i] = rdA(sa, 0, i);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) fb0[j] = rdB(sb, 0, j);
+#pragma unroll
+            for (int i = 0; i < LA; ++i) loadA(pa, kA, i);
+#pragma unroll
+            for (int i = 0; i < LB; ++i) loadB(pb, kB, i);
+            products(fa1, fb1);
+            // LDS reads first (the loads write LDS and keep their order after
+            // them), then two loads per product
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x010, 2, 0);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        region(fa0, fb0, fa1, fb1, sa, sb, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        region(fa1, fb1, fa0, fb0, sa, sb, 2);
+        __builtin_amdgcn_sched_barrier(0);
+        region(fa0, fb0, fa1, fb1, sa, sb, 3);
+        __builtin_amdgcn_sched_barrier(0);
+        // the reads of stage t have returned before the next barrier lets
+        // other waves refill it
+        wait_lds_reads();
+        sa ^= 1;
+        sb = sb + 1 == NSB ? 0 : sb + 1;
     }
-    store_tile<BM, BN, WM, WN>(a, acc, m0, n0, wm, wn, lane);
+    products(fa1, fb1);   // k-substep 3 of the last step
+    store_tile<BM, BN, 2, 2>(a, acc, m0, n0, wm, wn, lane);
 }
 
 template <int BM, int BN, int WM, int WN, int NS>
@@ -483,11 +542,13 @@ hipError_t launch_cfg(const GemmArgs& a, bool f32, hipStream_t s) {
 
 hipError_t launch_lmhead_gemm(const GemmArgs& a, bool hidden_f32, hipStream_t stream) {
     if (!hidden_f32 && a.K % 32 == 0) {
-        if (a.M > 128 && a.K % 64 == 0) {
+        // buffer offsets are 32-bit: the hidden rows and one lm_head tile
+        // must each span less than 4 GiB
+        const long hid_bytes = (long)((a.M + a.n_pred - 1) / a.n_pred) * a.L * a.K * 2;
+        if (a.M > 128 && a.K % 64 == 0 && hid_bytes < 0xFFFFFFFFL && 256L * a.K * 2 < 0x7FFFFFFFL) {
             const long tiles = (long)((a.M + 255) / 256) * ((a.N + 255) / 256);
             if (tiles > 0x7fffffffL) return hipErrorInvalidValue;
-            hipLaunchKernelGGL((lmhead_gemm_split<256, 256, 2, 4, 2, 3>), dim3((unsigned)tiles),
-                               dim3(512), 0, stream, a);
+            hipLaunchKernelGGL(lmhead_gemm_w4, dim3((unsigned)tiles), dim3(256), 0, stream, a);
             return hipGetLastError();
         }
         if (a.M > 128) return launch_dma<256, 256, 2, 4, 4>(a, stream);

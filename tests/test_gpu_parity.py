@@ -59,6 +59,10 @@ SMALL = {
     "dma_big_K32": lambda: make_small(20, 13, 32, 700, 8, top_k=3, seed=19),
     "dma_big_K96_bonus": lambda: make_small(23, 12, 96, 1000, 24, top_k=1, layout=BONUS_ANCHOR,
                                              conf=True, p_min=0.5, seed=20),
+    # four-wave GEMM path (M > 128, K % 64 == 0): ragged M and N tiles,
+    # several K steps; two K steps (loads past the end are clamped)
+    "w4_ragged_K320": lambda: make_small(37, 8, 320, 3000, 16, top_k=2, conf=True, p_min=0.4, seed=21),
+    "w4_two_ksteps": lambda: make_small(33, 9, 128, 1000, 8, top_k=1, layout=BONUS_ANCHOR, seed=22),
     "reduced_vocab": lambda: make_small(4, 7, 176, 4096, 64, top_k=4, layout=BONUS_ANCHOR,
                                         reachable=300, conf=True, p_min=0.5, conf_trend=True,
                                         seed=10),
