@@ -340,9 +340,10 @@ __global__ __launch_bounds__(64 * WM * WN) void lmhead_gemm_dma(GemmArgs a) {
 // lm_head descriptor covers exactly this tile's rows, so rows past N read as
 // zero). One barrier per K step, at its start. The step is cut into four
 // regions of 16 products; every region carries the LDS reads of the next
-// k-substep and the first one also the global->LDS loads of later stages, each
-// interleaved between the products (sched_group_barrier), so the matrix pipe
-// is never left waiting on an issue burst. Past the last K step the loads
+// k-substep, and the first three also the global->LDS loads of later stages
+// (A in the first, B split over the next two), each interleaved between the
+// products (sched_group_barrier), so the matrix pipe is never left waiting on
+// an issue burst. Past the last K step the loads
 // repeat the last step into stages that are not read again, which keeps the
 // step free of branches.
 // ---------------------------------------------------------------------------
@@ -431,20 +432,26 @@ __global__ __launch_bounds__(256) void lmhead_gemm_w4(GemmArgs a) {
 #pragma unroll
             for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16(fa[i], fb[j], acc[i][j]);
     };
-    // 16 products of (fa, fb) with the reads of k-substep ks into (nfa, nfb)
-    auto region = [&](const u32x4 (&fa)[FM], const u32x4 (&fb)[FN], u32x4 (&nfa)[FM], u32x4 (&nfb)[FN],
-                      int sa, int sb, int ks) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i) nfa[i] = rdA(sa, ks, i);
+    // Fragment reads of k-substep ks, in the order the products use them.
+    auto reads = [&](u32x4 (&nfa)[FM], u32x4 (&nfb)[FN], int sa, int sb, int ks) __attribute__((always_inline)) {
+        nfa[0] = rdA(sa, ks, 0);
 #pragma unroll
         for (int j = 0; j < FN; ++j) nfb[j] = rdB(sb, ks, j);
-        products(fa, fb);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        for (int i = 1; i < FM; ++i) nfa[i] = rdA(sa, ks, i);
+    };
+    // Issue order of a region: one LDS read after each of the first 8
+    // products, then nv (0, 4 or 8) loads spread over the last 8. The loads
+    // write LDS, so the compiler keeps them after the region's reads.
+    auto pattern = [&](int nv) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // one MFMA
+            if (q < 8)
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // one LDS read
+            else if (nv == 8 || (nv == 4 && q % 2 == 0))
+                __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);    // one load
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     };
 
     const int nK = K / BKS;
@@ -468,39 +475,35 @@ __global__ __launch_bounds__(256) void lmhead_gemm_w4(GemmArgs a) {
         wait_vmcnt<LB>();
         block_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        {
-            // k-substep 3 of step t - 1 (zero fragments at t = 0), the reads
-            // of (t, 0), and the loads A(t+1), B(t+2) into the stages of t - 1
-            const int pa = sa ^ 1, pb = sb == 0 ? NSB - 1 : sb - 1;
-            const int kA = min(t + 1, nK - 1) * BKS * 2, kB = min(t + 2, nK - 1) * BKS * 2;
+        // A(t+1) and B(t+2) go to the stages of t - 1
+        const int pa = sa ^ 1, pb = sb == 0 ? NSB - 1 : sb - 1;
+        const int kA = min(t + 1, nK - 1) * BKS * 2, kB = min(t + 2, nK - 1) * BKS * 2;
+        // region 1: k-substep 3 of step t - 1 (zero fragments at t = 0),
+        // reads of (t, 0), loads A(t+1)
+        reads(fa0, fb0, sa, sb, 0);
 #pragma unroll
-            for (int i = 0; i < FM; ++i) fa0[i] = rdA(sa, 0, i);
-#pragma unroll
-            for (int j = 0; j < FN; ++j) fb0[j] = rdB(sb, 0, j);
-#pragma unroll
-            for (int i = 0; i < LA; ++i) loadA(pa, kA, i);
-#pragma unroll
-            for (int i = 0; i < LB; ++i) loadB(pb, kB, i);
-            products(fa1, fb1);
-            // LDS reads first (the loads write LDS and keep their order after
-            // them), then two loads per product
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x010, 2, 0);
-            }
-        }
+        for (int i = 0; i < LA; ++i) loadA(pa, kA, i);
+        products(fa1, fb1);
+        pattern(8);
         __builtin_amdgcn_sched_barrier(0);
-        region(fa0, fb0, fa1, fb1, sa, sb, 1);
+        // region 2: (t, 0) products, reads of (t, 1), first half of B(t+2)
+        reads(fa1, fb1, sa, sb, 1);
+#pragma unroll
+        for (int i = 0; i < LB / 2; ++i) loadB(pb, kB, i);
+        products(fa0, fb0);
+        pattern(4);
         __builtin_amdgcn_sched_barrier(0);
-        region(fa1, fb1, fa0, fb0, sa, sb, 2);
+        // region 3: (t, 1) products, reads of (t, 2), second half of B(t+2)
+        reads(fa0, fb0, sa, sb, 2);
+#pragma unroll
+        for (int i = LB / 2; i < LB; ++i) loadB(pb, kB, i);
+        products(fa1, fb1);
+        pattern(4);
         __builtin_amdgcn_sched_barrier(0);
-        region(fa0, fb0, fa1, fb1, sa, sb, 3);
+        // region 4: (t, 2) products, reads of (t, 3)
+        reads(fa1, fb1, sa, sb, 3);
+        products(fa0, fb0);
+        pattern(0);
         __builtin_amdgcn_sched_barrier(0);
         // the reads of stage t have returned before the next barrier lets
         // other waves refill it
