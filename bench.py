@@ -28,9 +28,50 @@ METRIC = "drafted tokens/s (B×L Markov-chain proposals) at Qwen3.8-27B shape; %
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
+# HBM traffic of one lm_head GEMM launch at the throughput workload, from two
+# rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script, each scaled by
+# what the counter reads for a plain copy of known size (--calibrate-copy).
+# The figures and commands are in profiles/lmhead_gemm_qwen38_27b_throughput_traffic.txt.
+# They describe the kernel source whose SHA-256 is recorded here and are not
+# reported for any other source or workload.
+GEMM_TRAFFIC = {
+    "workload": "qwen38_27b_throughput",
+    "source_sha256": "c6047edb2e7bead590f9655377786901b29c52f02ea42c52d92ab8159fcbc7cf",
+    "bytes": 5633881750,
+}
+
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def gemm_source_sha256() -> str:
+    import hashlib
+    path = os.path.join(ROOT, "dspark_block_drafter_amd", "csrc", "lmhead_gemm.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload: str):
+    t = GEMM_TRAFFIC
+    if t["bytes"] is None or workload != t["workload"] or gemm_source_sha256() != t["source_sha256"]:
+        return None
+    return t["bytes"]
+
+
+def calibrate_copy(mib: int, reps: int) -> int:
+    """A plain device-to-device copy of a known size, for scaling the HBM byte
+    counters (read `mib` MiB, write `mib` MiB per launch)."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.randn(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n * 4, "launches": reps}), flush=True)
+    return 0
 
 
 def cpu_baseline(inp, blocks: int) -> dict:
@@ -55,11 +96,16 @@ def main() -> int:
     ap.add_argument("--workload", default="qwen38_27b_throughput")
     ap.add_argument("--cpu-blocks", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the proposal step is built and measured on a "
               "single MI355X; run it with --gpus 1", file=sys.stderr)
         return 2
+
+    if args.calibrate_copy > 0:
+        return calibrate_copy(args.calibrate_copy, max(args.steps, 1))
 
     import torch
 
@@ -139,7 +185,8 @@ def main() -> int:
                    "top_k": cfg.top_k, "p_min": cfg.p_min, "layout": cfg.layout,
                    "drafted_tokens_per_step": cfg.drafted_tokens},
         "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": gemm_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": gemm_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": measured_traffic(cfg.name),
                      "kernel": "lmhead_gemm", "us": gemm_ms * 1e3},
         "roofline_chain": {"bound": "hbm", "achieved": chain_gbs, "peak": PEAK_HBM_GBS,
                            "unit": "GB/s", "frac": chain_gbs / PEAK_HBM_GBS,
