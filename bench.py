@@ -96,6 +96,8 @@ def main() -> int:
     ap.add_argument("--workload", default="qwen38_27b_throughput")
     ap.add_argument("--cpu-blocks", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--d2t", action="store_true",
+                    help="run the workload's reduced-vocabulary form (dspark_propose_d2t)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -117,15 +119,33 @@ def main() -> int:
     t0 = time.perf_counter()
     inp = make_inputs(cfg)
     log(f"inputs for {cfg.name} generated in {time.perf_counter() - t0:.1f} s")
-    d = to_device(inp)
-    out = dsp.Outputs(cfg.B, cfg.L, cfg.V, cfg.top_k, cfg.layout, "cuda:0")
     stream = torch.cuda.current_stream()
-    torch.cuda.synchronize()
+    if args.d2t:
+        from devutil import to_device_reduced
+        from synthetic import reduce_vocab
+        if inp.reachable is None:
+            print(f"--d2t needs a workload with a reduced vocabulary; {cfg.name} has none",
+                  file=sys.stderr)
+            return 2
+        red = reduce_vocab(inp)
+        d = to_device_reduced(red)
+        N = red.D
+        out = dsp.Outputs(cfg.B, cfg.L, N, cfg.top_k, cfg.layout, "cuda:0")
 
-    def step():
-        dsp.propose(d["hidden"], d["lm_head"], d["markov_w1"], d["markov_w2"], d["anchors"],
-                    layout=cfg.layout, top_k=cfg.top_k, p_min=cfg.p_min,
-                    lm_head_bias=d["lm_head_bias"], conf_w=d["conf_w"], out=out, stream=stream)
+        def step():
+            dsp.propose_d2t(d["hidden"], d["lm_head"], d["d2t"], d["markov_w1"], d["markov_w2"],
+                            d["anchors"], vocab=cfg.V, layout=cfg.layout, top_k=cfg.top_k,
+                            p_min=cfg.p_min, conf_w=d["conf_w"], out=out, stream=stream)
+    else:
+        d = to_device(inp)
+        N = cfg.V
+        out = dsp.Outputs(cfg.B, cfg.L, cfg.V, cfg.top_k, cfg.layout, "cuda:0")
+
+        def step():
+            dsp.propose(d["hidden"], d["lm_head"], d["markov_w1"], d["markov_w2"], d["anchors"],
+                        layout=cfg.layout, top_k=cfg.top_k, p_min=cfg.p_min,
+                        lm_head_bias=d["lm_head_bias"], conf_w=d["conf_w"], out=out, stream=stream)
+    torch.cuda.synchronize()
 
     for _ in range(args.warmup):
         step()
@@ -145,25 +165,39 @@ def main() -> int:
     log(f"timed {args.steps} steps: {ms:.3f} ms/step (events), {1e3 * wall / args.steps:.3f} ms/step (wall)")
     assert dsp.read_flags(out) == 0
 
-    # Per-kernel split: the same kernels through dspark_logits + dspark_chain.
+    # Per-kernel split: the same projection through dspark_logits, then the
+    # chain through dspark_chain (the d2t form has no separate chain entry:
+    # its chain time is the step minus the projection).
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for e in evs:
         e[0].record(stream)
-        dsp.logits(d["hidden"], d["lm_head"], layout=cfg.layout, lm_head_bias=d["lm_head_bias"],
-                   out=out.logits, stream=stream)
+        dsp.logits(d["hidden"], d["lm_head"], layout=cfg.layout,
+                   lm_head_bias=None if args.d2t else d["lm_head_bias"], out=out.logits,
+                   stream=stream)
         e[1].record(stream)
-        dsp.chain(out.logits, d["markov_w1"], d["markov_w2"], d["anchors"], B=cfg.B, L=cfg.L,
-                  layout=cfg.layout, top_k=cfg.top_k, p_min=cfg.p_min, hidden=d["hidden"],
-                  conf_w=d["conf_w"], out=out, stream=stream)
+        if not args.d2t:
+            dsp.chain(out.logits, d["markov_w1"], d["markov_w2"], d["anchors"], B=cfg.B, L=cfg.L,
+                      layout=cfg.layout, top_k=cfg.top_k, p_min=cfg.p_min, hidden=d["hidden"],
+                      conf_w=d["conf_w"], out=out, stream=stream)
         e[2].record(stream)
     torch.cuda.synchronize()
     gemm_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    chain_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    chain_ms = (ms - gemm_ms) if args.d2t else sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     log(f"lm_head GEMM {gemm_ms * 1e3:.1f} us, chain+finalize {chain_ms * 1e3:.1f} us")
 
-    M, H, V, r, B, n = cfg.B * cfg.n_pred, cfg.H, cfg.V, cfg.r, cfg.B, cfg.n_pred
+    M, H, V, r, B, n = cfg.B * cfg.n_pred, cfg.H, N, cfg.r, cfg.B, cfg.n_pred
     flops = 2.0 * M * H * V
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
+    gemm_bytes = V * H * 2 + M * H * 2 + M * V * 4
+    # the projection is matrix-bound above the ridge point (peak FLOP/s over
+    # peak bytes/s, 312 FLOP/B), HBM-bound below it
+    if flops / gemm_bytes > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        gemm_roof = {"bound": "mfma", "achieved": gemm_tflops, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": gemm_tflops / PEAK_BF16_TFLOPS}
+    else:
+        gemm_gbs = gemm_bytes / (gemm_ms * 1e-3) / 1e9
+        gemm_roof = {"bound": "hbm", "achieved": gemm_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gemm_gbs / PEAK_HBM_GBS}
     # chain: per slot the B logits rows and markov_w2 are streamed, plus B rank-r gathers
     chain_bytes = n * (B * V * 4 + V * r * 2 + B * r * 2)
     chain_gbs = chain_bytes / (chain_ms * 1e-3) / 1e9
@@ -181,12 +215,12 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "B": cfg.B, "L": cfg.L, "H": H, "V": V, "r": r,
+        "config": {"workload": cfg.name, "B": cfg.B, "L": cfg.L, "H": H, "V": cfg.V, "r": r,
                    "top_k": cfg.top_k, "p_min": cfg.p_min, "layout": cfg.layout,
-                   "drafted_tokens_per_step": cfg.drafted_tokens},
-        "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": gemm_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": measured_traffic(cfg.name),
+                   "drafted_tokens_per_step": cfg.drafted_tokens,
+                   **({"d2t_draft_vocab": N} if args.d2t else {})},
+        "roofline": {**gemm_roof,
+                     "traffic": None if args.d2t else measured_traffic(cfg.name),
                      "kernel": "lmhead_gemm", "us": gemm_ms * 1e3},
         "roofline_chain": {"bound": "hbm", "achieved": chain_gbs, "peak": PEAK_HBM_GBS,
                            "unit": "GB/s", "frac": chain_gbs / PEAK_HBM_GBS,

@@ -31,12 +31,13 @@ ERR_HIP = -4
 
 FLAG_BAD_ANCHOR = 1
 FLAG_INTERNAL = 2
+FLAG_BAD_D2T = 4
 
 MAX_TOP_K = 16
 MAX_RANK = 256
 
 EXPORTS = ("dspark_workspace_bytes", "dspark_propose", "dspark_logits", "dspark_chain",
-           "dspark_read_flags", "dspark_status_string")
+           "dspark_propose_d2t", "dspark_read_flags", "dspark_status_string")
 
 
 class DsparkError(RuntimeError):
@@ -73,6 +74,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                  _i, _i, _i, _i, _i, _i, _i, _f,
                                  _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.dspark_chain.restype = _i
+    lib.dspark_propose_d2t.argtypes = [_vp, _i, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       _i, _i, _i, _i, _i, _i, _i, _i, _f,
+                                       _vp, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp]
+    lib.dspark_propose_d2t.restype = _i
     lib.dspark_read_flags.argtypes = [_vp, ctypes.POINTER(ctypes.c_uint32), _vp]
     lib.dspark_read_flags.restype = _i
     lib.dspark_status_string.argtypes = [_i]
@@ -186,6 +191,38 @@ def propose(hidden, lm_head, markov_w1, markov_w2, anchors, *, layout="anchor_fi
         _ptr(out.lengths), _stream(hidden, stream))
     if st != OK:
         raise DsparkError(st, "dspark_propose")
+    return out
+
+
+def propose_d2t(hidden, lm_head, d2t, markov_w1, markov_w2, anchors, *, vocab: int,
+                layout="anchor_first", top_k=1, p_min=0.0, conf_w=None,
+                out: Optional[Outputs] = None, stream=None) -> Outputs:
+    """Run dspark_propose_d2t: a draft head over D draft ids (``lm_head`` [D, H],
+    ``markov_w2`` [D, r]) whose ids map to target ids through ``d2t`` (int64 [D],
+    strictly increasing, in [0, vocab)); ``markov_w1`` is [vocab, r]. The Outputs
+    must be sized for D columns; tokens and candidates come back as target ids."""
+    torch = _torch()
+    lib = load_library()
+    B, L, H = hidden.shape
+    D = lm_head.shape[0]
+    r = 0 if markov_w1 is None else markov_w1.shape[1]
+    _check_dev("hidden", hidden, hidden.dtype)
+    _check_dev("lm_head", lm_head, torch.bfloat16, (D, H))
+    _check_dev("d2t", d2t, torch.int64, (D,))
+    _check_dev("markov_w1", markov_w1, torch.bfloat16, (vocab, r))
+    _check_dev("markov_w2", markov_w2, torch.bfloat16, (D, r))
+    _check_dev("conf_w", conf_w, torch.bfloat16, (H,))
+    _check_dev("anchors", anchors, torch.int32, (B,))
+    if out is None:
+        out = Outputs(B, L, D, top_k, layout, hidden.device)
+    st = lib.dspark_propose_d2t(
+        _ptr(hidden), _hidden_dtype(hidden), _ptr(lm_head), _ptr(d2t), _ptr(markov_w1),
+        _ptr(markov_w2), _ptr(conf_w), _ptr(anchors), B, L, H, int(vocab), D, r,
+        LAYOUTS[layout], top_k, float(p_min), _ptr(out.logits), _ptr(out.workspace),
+        out.workspace.numel(), _ptr(out.tokens), _ptr(out.candidates), _ptr(out.cand_logits),
+        _ptr(out.conf), _ptr(out.lengths), _stream(hidden, stream))
+    if st != OK:
+        raise DsparkError(st, "dspark_propose_d2t")
     return out
 
 

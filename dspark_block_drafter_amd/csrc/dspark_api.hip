@@ -72,11 +72,13 @@ int check_chain_args(int V, int r, int top_k, float p_min, const void* w1, const
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP; }
 
+// The chain over V columns; with d2t (a reduced draft vocabulary) column c is
+// target id d2t[c] and previous tokens index markov_w1 in [0, vocab).
 int run_chain(const float* logits, const void* hidden, int hidden_dtype, const uint16_t* w1,
-              const uint16_t* w2, const uint16_t* conf_w, const int32_t* anchors, int B, int L,
-              int H, int V, int r, int layout, int top_k, float p_min, void* workspace,
-              int32_t* tokens, int32_t* candidates, float* cand_logits, float* conf,
-              int32_t* lengths, hipStream_t stream) {
+              const uint16_t* w2, const int64_t* d2t, int vocab, const uint16_t* conf_w,
+              const int32_t* anchors, int B, int L, int H, int V, int r, int layout, int top_k,
+              float p_min, void* workspace, int32_t* tokens, int32_t* candidates,
+              float* cand_logits, float* conf, int32_t* lengths, hipStream_t stream) {
     const int i_first = first_pred(layout);
     const int n_pred = L - i_first;
     const Layout wl = workspace_layout(B, n_pred, V, top_k);
@@ -86,6 +88,8 @@ int run_chain(const float* logits, const void* hidden, int hidden_dtype, const u
     c.logits = logits;
     c.w1 = w1;
     c.w2 = w2;
+    c.d2t = d2t;
+    c.vocab = vocab;
     c.anchors = anchors;
     c.winners = reinterpret_cast<unsigned long long*>(ws + wl.winners_off);
     c.partials = top_k > 1 ? reinterpret_cast<unsigned long long*>(ws + wl.partials_off) : nullptr;
@@ -105,6 +109,8 @@ int run_chain(const float* logits, const void* hidden, int hidden_dtype, const u
     FinalArgs f;
     f.winners = c.winners;
     f.partials = c.partials;
+    f.d2t = d2t;
+    f.V = V;
     f.hidden = hidden;
     f.conf_w = conf_w;
     f.tokens = tokens;
@@ -177,9 +183,9 @@ int dspark_chain(const float* logits, const void* hidden, int hidden_dtype,
     if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return DSPARK_ERR_WORKSPACE;
     if (workspace_bytes < dspark_workspace_bytes(B, L, V, top_k, layout)) return DSPARK_ERR_WORKSPACE;
     if (!aligned16(logits)) return DSPARK_ERR_UNSUPPORTED;
-    return run_chain(logits, hidden, hidden_dtype, markov_w1, markov_w2, conf_w, anchors, B, L, H,
-                     V, r, layout, top_k, p_min, workspace, tokens, candidates, cand_logits, conf,
-                     lengths, static_cast<hipStream_t>(stream));
+    return run_chain(logits, hidden, hidden_dtype, markov_w1, markov_w2, nullptr, V, conf_w,
+                     anchors, B, L, H, V, r, layout, top_k, p_min, workspace, tokens, candidates,
+                     cand_logits, conf, lengths, static_cast<hipStream_t>(stream));
 }
 
 int dspark_propose(const void* hidden, int hidden_dtype, const uint16_t* lm_head,
@@ -205,9 +211,39 @@ int dspark_propose(const void* hidden, int hidden_dtype, const uint16_t* lm_head
     st = dspark_logits(hidden, hidden_dtype, lm_head, lm_head_bias, B, L, H, V, layout, logits,
                        stream);
     if (st != DSPARK_OK) return st;
-    return run_chain(logits, hidden, hidden_dtype, markov_w1, markov_w2, conf_w, anchors, B, L, H,
-                     V, r, layout, top_k, p_min, workspace, tokens, candidates, cand_logits, conf,
-                     lengths, static_cast<hipStream_t>(stream));
+    return run_chain(logits, hidden, hidden_dtype, markov_w1, markov_w2, nullptr, V, conf_w,
+                     anchors, B, L, H, V, r, layout, top_k, p_min, workspace, tokens, candidates,
+                     cand_logits, conf, lengths, static_cast<hipStream_t>(stream));
+}
+
+int dspark_propose_d2t(const void* hidden, int hidden_dtype, const uint16_t* lm_head,
+                       const int64_t* d2t, const uint16_t* markov_w1, const uint16_t* markov_w2,
+                       const uint16_t* conf_w, const int32_t* anchors, int B, int L, int H, int V,
+                       int D, int r, int layout, int top_k, float p_min, float* logits,
+                       void* workspace, size_t workspace_bytes, int32_t* tokens,
+                       int32_t* candidates, float* cand_logits, float* conf, int32_t* lengths,
+                       void* stream) {
+    // the projection and the chain run over the D draft ids
+    int st = check_sizes(B, L, H, D, layout, hidden_dtype);
+    if (st != DSPARK_OK) return st;
+    if (V <= 0 || D > V) return DSPARK_ERR_INVALID_ARG;
+    if (V >= 0x7fffffff - 1024) return DSPARK_ERR_UNSUPPORTED;
+    st = check_chain_args(D, r, top_k, p_min, markov_w1, markov_w2);
+    if (st != DSPARK_OK) return st;
+    if (!hidden || !lm_head || !d2t || !logits || !anchors || !tokens || !candidates || !lengths)
+        return DSPARK_ERR_INVALID_ARG;
+    if (!aligned16(hidden) || !aligned16(lm_head) || !aligned16(logits) ||
+        (conf_w && !aligned16(conf_w)) || (reinterpret_cast<uintptr_t>(d2t) & 7u) != 0)
+        return DSPARK_ERR_UNSUPPORTED;
+    if (!workspace) return DSPARK_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return DSPARK_ERR_WORKSPACE;
+    if (workspace_bytes < dspark_workspace_bytes(B, L, D, top_k, layout)) return DSPARK_ERR_WORKSPACE;
+
+    st = dspark_logits(hidden, hidden_dtype, lm_head, nullptr, B, L, H, D, layout, logits, stream);
+    if (st != DSPARK_OK) return st;
+    return run_chain(logits, hidden, hidden_dtype, markov_w1, markov_w2, d2t, V, conf_w, anchors,
+                     B, L, H, D, r, layout, top_k, p_min, workspace, tokens, candidates,
+                     cand_logits, conf, lengths, static_cast<hipStream_t>(stream));
 }
 
 int dspark_read_flags(const void* workspace, uint32_t* flags, void* stream) {

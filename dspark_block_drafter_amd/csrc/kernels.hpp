@@ -45,16 +45,25 @@ inline int chain_workgroups_max(int V) {
     return (V + kChainTileV - 1) / kChainTileV;
 }
 
+// Flags word bits (the public values of DSPARK_FLAG_*).
+constexpr uint32_t kFlagBadAnchor = 1u, kFlagInternal = 2u, kFlagBadD2t = 4u;
+
+// The chain runs over V columns. Without a d2t table a column is a
+// vocabulary id; with one (a reduced draft vocabulary), column c is draft id c
+// and stands for target id d2t[c], and previous tokens (anchors included) are
+// target ids in [0, vocab) that index markov_w1.
 struct ChainArgs {
     const float* logits;       // [B * n_pred, V]
-    const uint16_t* w1;        // [V, r] bf16 bits (nullptr iff r == 0)
+    const uint16_t* w1;        // [vocab, r] bf16 bits (nullptr iff r == 0)
     const uint16_t* w2;        // [V, r] bf16 bits
+    const int64_t* d2t;        // [V] target id of each column, or nullptr (identity)
     const int32_t* anchors;    // [B]
     unsigned long long* winners;   // [n_pred, B] running argmax keys
     unsigned long long* partials;  // [n_pred, B, nwg, top_k] per-workgroup top-k keys (top_k > 1)
     uint32_t* flags;
     int32_t* lengths;          // [B], set to n_pred here, cut by the confidence head later
     int B, V, r, n_pred, top_k, nwg;
+    int vocab;                 // target vocabulary size (== V without d2t)
 };
 hipError_t launch_chain_init(const ChainArgs& a, hipStream_t stream);
 hipError_t launch_chain_step(const ChainArgs& a, int j, hipStream_t stream);
@@ -64,6 +73,7 @@ struct FinalArgs {
     const unsigned long long* partials;
     const void* hidden;        // [B, L, H] (confidence head only)
     const uint16_t* conf_w;    // [H] or nullptr
+    const int64_t* d2t;        // as in ChainArgs: tokens and candidates are mapped through it
     int32_t* tokens;           // [B, n_pred]
     int32_t* candidates;       // [B, n_pred, top_k]
     float* cand_logits;        // [B, n_pred, top_k] or nullptr
@@ -71,6 +81,7 @@ struct FinalArgs {
     int32_t* lengths;          // [B]
     uint32_t* flags;
     int B, L, H, n_pred, i_first, top_k, nwg;
+    int V;                     // chain columns (keys outside [0, V) are never mapped)
     int hidden_f32;
     float p_min;
 };

@@ -42,25 +42,44 @@ __global__ __launch_bounds__(256) void chain_init(u64* winners, int n, uint32_t*
 
 // ---- pieces shared by the two step kernels ----------------------------------
 
+// Target id of chain column c: the column itself, or d2t[c] for a reduced
+// draft vocabulary (llama.cpp PR #26275, rework commit message: d2t holds
+// absolute target ids and the draft logits are scattered at run time).
+__device__ __forceinline__ long column_token(const int64_t* d2t, int c) {
+    return d2t ? (long)d2t[c] : (long)c;
+}
+
+// The previous token of block b for slot j: the anchor, or the target id of
+// the previous slot's argmax column. A value outside [0, vocab) is replaced
+// by 0 and reported (when `report`) in the flags word.
+__device__ __forceinline__ int prev_token(const ChainArgs& a, int j, int b, bool report) {
+    long t;
+    uint32_t bad;
+    if (j == 0) {
+        t = a.anchors[b];
+        bad = kFlagBadAnchor;
+    } else {
+        const int c = key_id(a.winners[(long)(j - 1) * a.B + b]);
+        t = (c >= 0 && c < a.V) ? column_token(a.d2t, c) : -1;
+        bad = kFlagBadD2t;
+    }
+    if (t >= 0 && t < a.vocab) return (int)t;
+    if (report) atomicOr(a.flags, bad);
+    return 0;
+}
+
 // prev_b for slot j (anchor, or the previous slot's argmax) and the lane's
 // share of markov_w1[prev_b] as MFMA B operand: u[nb][s] holds
 // W1[prev][16 s + 8 (lane / 32) .. + 8] for block bbase + 32 nb + lane % 32.
 template <int NB, int RS>
 __device__ __forceinline__ void gather_w1(const ChainArgs& a, int j, int bbase, int lrow, int lhalf,
                                           u32x4 (&u)[NB][RS], int (&bl)[NB]) {
-    const int B = a.B, V = a.V, r = a.r;
+    const int B = a.B, r = a.r;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         const int b = bbase + nb * 32 + lrow;
         bl[nb] = b;
-        int prev = 0;
-        if (b < B) {
-            prev = (j == 0) ? a.anchors[b] : key_id(a.winners[(long)(j - 1) * B + b]);
-            if (prev < 0 || prev >= V) {
-                if (j == 0) atomicOr(a.flags, 1u);
-                prev = 0;
-            }
-        }
+        const int prev = b < B ? prev_token(a, j, b, true) : 0;
 #pragma unroll
         for (int s = 0; s < RS; ++s) {
             const int k0 = s * 16 + lhalf * 8;
@@ -220,14 +239,7 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
 
     // Previous token of this lane's block (anchor, or the last slot's argmax).
     const int bme = bbase + nbw * 32 + lrow;
-    int prev = 0;
-    if (bme < B && nbw < NB) {
-        prev = (j == 0) ? a.anchors[bme] : key_id(a.winners[(long)(j - 1) * B + bme]);
-        if (prev < 0 || prev >= V) {
-            if (j == 0 && vb == 0) atomicOr(a.flags, 1u);
-            prev = 0;
-        }
-    }
+    const int prev = (bme < B && nbw < NB) ? prev_token(a, j, bme, vb == 0) : 0;
     // First NS - 1 tiles in flight, then the markov_w1 rows of prev (MFMA B
     // operand). One full wait before the loop: the loop then only ever waits
     // for ring stages (a register load still in flight there would make every
@@ -455,14 +467,22 @@ __global__ __launch_bounds__(256) void chain_step_direct(ChainArgs a, int j) {
         }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            f32x16 acc = f32x16{};
+            // The logits enter the MFMA as accumulator input, as in the
+            // pipelined kernel, so both kernels round the same sums.
+            const int b = bl[nb];
+            const float* row = a.logits + ((long)min(b, B - 1) * a.n_pred + j) * V;
+            f32x16 acc;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int vq = v0 + 8 * q + 4 * lhalf;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[4 * q + e] = (vq + e < V) ? row[vq + e] : 0.0f;
+            }
             if (r > 0) {
 #pragma unroll
                 for (int s = 0; s < RS; ++s) acc = mfma32x32x16(w[s], u[nb][s], acc);
             }
-            const int b = bl[nb];
             if (b >= B) continue;
-            const float* row = a.logits + ((long)b * a.n_pred + j) * V;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int vq = v0 + 8 * q + 4 * lhalf;
@@ -470,7 +490,7 @@ __global__ __launch_bounds__(256) void chain_step_direct(ChainArgs a, int j) {
                 for (int e = 0; e < 4; ++e) {
                     const int v = vq + e;
                     if (v < V) {
-                        const u64 key = make_key(row[v] + acc[4 * q + e], v);
+                        const u64 key = make_key(acc[4 * q + e], v);
                         if (key > list[nb][KL - 1]) topk_insert<KL>(list[nb], key);
                     }
                 }
@@ -481,6 +501,12 @@ __global__ __launch_bounds__(256) void chain_step_direct(ChainArgs a, int j) {
 }
 
 // ---- final assembly: one workgroup per (slot, block) --------------------------
+
+// Output id of a key: the target id of its column (the column without d2t).
+__device__ __forceinline__ int final_token(const FinalArgs& a, u64 key) {
+    const int c = key_id(key);
+    return (c >= 0 && c < a.V) ? (int)column_token(a.d2t, c) : c;
+}
 
 // Candidates of slot j of block b from the per-workgroup partial lists, then
 // the confidence of that slot; lengths[b] (preset to n_pred) is lowered to j
@@ -498,8 +524,9 @@ __global__ __launch_bounds__(256) void finalize(FinalArgs a) {
 
     if (k == 1) {
         if (threadIdx.x == 0) {
-            a.tokens[o] = key_id(win);
-            a.candidates[o] = key_id(win);
+            const int t = final_token(a, win);
+            a.tokens[o] = t;
+            a.candidates[o] = t;
             if (a.cand_logits) a.cand_logits[o] = key_score(win);
         }
     } else {
@@ -530,12 +557,12 @@ __global__ __launch_bounds__(256) void finalize(FinalArgs a) {
             for (int w = 1; w < kWaves; ++w)
 #pragma unroll
                 for (int i = 0; i < KL; ++i) topk_insert<KL>(list, s_list[w][i]);
-            a.tokens[o] = key_id(win);
-            if (list[0] != win) atomicOr(a.flags, 2u);  // internal consistency check
+            a.tokens[o] = final_token(a, win);
+            if (list[0] != win) atomicOr(a.flags, kFlagInternal);  // internal consistency check
 #pragma unroll
             for (int i = 0; i < KL; ++i) {
                 if (i < k) {
-                    a.candidates[o * k + i] = key_id(list[i]);
+                    a.candidates[o * k + i] = final_token(a, list[i]);
                     if (a.cand_logits) a.cand_logits[o * k + i] = key_score(list[i]);
                 }
             }

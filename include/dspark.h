@@ -92,6 +92,7 @@ typedef enum {
 /* Device-side flags accumulated in the workspace by a call. */
 #define DSPARK_FLAG_BAD_ANCHOR 1u   /* an anchor was outside [0, V)                      */
 #define DSPARK_FLAG_INTERNAL 2u     /* the candidate merge disagreed with the chain's argmax */
+#define DSPARK_FLAG_BAD_D2T 4u      /* a d2t entry the chain followed was outside [0, V)  */
 
 /* Limits checked by every entry point. */
 #define DSPARK_MAX_TOP_K 16
@@ -169,8 +170,49 @@ int dspark_chain(const float* logits, const void* hidden, int hidden_dtype,
                  int32_t* lengths, void* stream);
 
 /*
+ * The proposal step of a draft with a reduced output vocabulary: its head
+ * scores D <= V draft ids, and the int64 table d2t gives the absolute target
+ * id of each draft id. The projection and the chain run over the D draft
+ * ids only; tokens and candidates come out as target ids. This is the
+ * run-time scatter of llama.cpp PR #26275 "dspark: support speculators-format
+ * checkpoints" (rework commit message: d2t holds I64 absolute target ids, as
+ * for EAGLE3, and the draft logits are scattered at run time instead of
+ * expanding lm_head / markov_w2 and adding a -1e9 bias at conversion; "Format
+ * differences": draft_vocab_size < vocab_size with a d2t table). It computes
+ * what dspark_propose computes on the expanded form -- lm_head and markov_w2
+ * rows placed at d2t[i], zero rows elsewhere, bias -1e9 off the table --
+ * bit for bit on tokens, candidates, cand_logits, conf and lengths.
+ *
+ *   lm_head       DEVICE bf16 [D, H]: the draft head, one row per draft id.
+ *   d2t           DEVICE int64 [D], 8-byte aligned: strictly increasing target
+ *                 ids in [0, V) (so ties between draft ids go to the lower
+ *                 target id, as in the expanded form). Entries are range
+ *                 checked when the chain follows them: an entry outside
+ *                 [0, V) is replaced by 0 and raises DSPARK_FLAG_BAD_D2T;
+ *                 the order is not checked.
+ *   markov_w1     DEVICE bf16 [V, r]: indexed by the previous token, a
+ *                 target id (anchors are target ids).
+ *   markov_w2     DEVICE bf16 [D, r]: draft rows.
+ *   V, D          target and draft vocabulary sizes, 1 <= D <= V;
+ *                 top_k <= min(D, DSPARK_MAX_TOP_K).
+ *   logits        DEVICE fp32 [B*n_pred, D] output: draft-id projections (no
+ *                 bias).
+ *   workspace     at least dspark_workspace_bytes(B, L, D, top_k, layout).
+ *   tokens, candidates, cand_logits, conf, lengths: as in dspark_propose,
+ *                 with target ids.
+ * Every other argument is as in dspark_propose. Returns a dspark_status.
+ */
+int dspark_propose_d2t(const void* hidden, int hidden_dtype, const uint16_t* lm_head,
+                       const int64_t* d2t, const uint16_t* markov_w1, const uint16_t* markov_w2,
+                       const uint16_t* conf_w, const int32_t* anchors, int B, int L, int H, int V,
+                       int D, int r, int layout, int top_k, float p_min, float* logits,
+                       void* workspace, size_t workspace_bytes, int32_t* tokens,
+                       int32_t* candidates, float* cand_logits, float* conf, int32_t* lengths,
+                       void* stream);
+
+/*
  * Copies the flags word of `workspace` (written by the last dspark_propose /
- * dspark_chain on it) to *flags after `stream` has drained; this call does
+ * dspark_propose_d2t / dspark_chain on it) to *flags after `stream` has drained; this call does
  * synchronise the stream. Returns a dspark_status.
  */
 int dspark_read_flags(const void* workspace, uint32_t* flags, void* stream);

@@ -46,6 +46,7 @@ _u16p = ctypes.POINTER(ctypes.c_uint16)
 _f32p = ctypes.POINTER(ctypes.c_float)
 _f64p = ctypes.POINTER(ctypes.c_double)
 _i32p = ctypes.POINTER(ctypes.c_int32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
 
@@ -75,6 +76,13 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
                                          _i, _i, _i, _i, _i, _i, ctypes.c_float, _i, _f64p,
                                          _i32p, _i32p, _f32p, _f32p, _i32p]
     lib.oracle_propose_block.restype = _i
+    lib.oracle_block_chain_d2t.argtypes = [_f64p, _u16p, _u16p, _i64p, _i, _i, _i, _i, _i, _i,
+                                           _i32p, _i32p, _f32p]
+    lib.oracle_block_chain_d2t.restype = _i
+    lib.oracle_propose_block_d2t.argtypes = [_vp, _i, _u16p, _i64p, _u16p, _u16p, _u16p, _i32p,
+                                             _i, _i, _i, _i, _i, _i, _i, ctypes.c_float, _i,
+                                             _f64p, _i32p, _i32p, _f32p, _f32p, _i32p]
+    lib.oracle_propose_block_d2t.restype = _i
     return lib
 
 
@@ -201,6 +209,29 @@ class Oracle:
             _p(length, _i32p))
         if st != 0:
             raise ValueError("oracle_propose_block rejected its arguments")
+        return {"logits": z, "tokens": tokens, "candidates": cand, "cand_logits": cval,
+                "conf": conf, "length": int(length[0])}
+
+    def propose_block_d2t(self, red, b: int, keep_logits: bool = True) -> dict:
+        """Block b of a reduced-vocabulary input (``synthetic.ReducedInputs``)."""
+        c = red.cfg
+        n, k, D = c.n_pred, c.top_k, red.D
+        z = np.empty((n, D), dtype=np.float64) if keep_logits else None
+        tokens = np.empty(n, dtype=np.int32)
+        cand = np.empty((n, k), dtype=np.int32)
+        cval = np.empty((n, k), dtype=np.float32)
+        conf = np.empty(n, dtype=np.float32)
+        length = np.zeros(1, dtype=np.int32)
+        st = self.lib.oracle_propose_block_d2t(
+            red.hidden.ctypes.data, int(red.hidden_f32), _p(red.lm_head, _u16p), _p(red.d2t, _i64p),
+            _p(red.markov_w1, _u16p), _p(red.markov_w2, _u16p), _p(red.conf_w, _u16p),
+            _p(red.anchors, _i32p), c.L, c.H, c.V, D, c.r, c.i_first_pred, k,
+            ctypes.c_float(c.p_min), b,
+            _p(z, _f64p) if z is not None else ctypes.cast(None, _f64p),
+            _p(tokens, _i32p), _p(cand, _i32p), _p(cval, _f32p), _p(conf, _f32p),
+            _p(length, _i32p))
+        if st != 0:
+            raise ValueError("oracle_propose_block_d2t rejected its arguments")
         return {"logits": z, "tokens": tokens, "candidates": cand, "cand_logits": cval,
                 "conf": conf, "length": int(length[0])}
 

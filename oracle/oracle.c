@@ -30,6 +30,15 @@
  *     add confidence-based draft pruning for DSpark" and "dspark: fold
  *     conf_min into p_min").
  *
+ * Reduced draft vocabulary: the draft head scores D draft ids and the int64
+ * table d2t gives the absolute target id of each; the draft logits are
+ * scattered to those target ids at run time (llama.cpp PR #26275, rework
+ * commit message; "Format differences": draft_vocab_size < vocab_size with a
+ * d2t table). The chain then runs over the draft ids: the Markov bias of
+ * draft id i is markov_w2[i] . markov_w1[prev] with prev a target id, and the
+ * chosen draft ids are reported as target ids. Every target id off the table
+ * has no score, so it can never be chosen.
+ *
  * Block layouts: anchor-first (every slot predicts; i_first_pred = 0) and the
  * 1+N bonus-anchor layout (slot 0 holds the bonus token and is never read;
  * i_first_pred = 1) (llama.cpp PR #26275, first commit message and
@@ -234,6 +243,51 @@ int oracle_block_chain(const double* z, const uint16_t* w1, const uint16_t* w2, 
     return st;
 }
 
+/* The chain of one block of a reduced draft vocabulary over its draft
+ * projections z [n_pred][D]: draft id i scores float(z_j[i] + sum_k
+ * w2[i][k] * w1[prev][k]) with w1 [V][r] indexed by the target id prev and
+ * w2 [D][r] by draft id; argmax and top-k run over draft ids (lowest draft id
+ * on ties) and are reported through d2t; the next prev is d2t[argmax]. */
+int oracle_block_chain_d2t(const double* z, const uint16_t* w1, const uint16_t* w2,
+                           const int64_t* d2t, int V, int D, int r, int anchor, int n_pred,
+                           int top_k, int32_t* tokens, int32_t* cand, float* cand_val)
+{
+    if (anchor < 0 || anchor >= V || D < 1 || D > V || n_pred <= 0 || top_k < 1 || top_k > D ||
+        r < 0)
+        return ORACLE_ERR;
+    for (int i = 0; i < D; ++i)
+        if (d2t[i] < 0 || d2t[i] >= V)
+            return ORACLE_ERR;
+    float* zp = (float*)malloc(sizeof(float) * (size_t)D);
+    int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * (size_t)top_k);
+    if (!zp || !idx) {
+        free(zp);
+        free(idx);
+        return ORACLE_ERR;
+    }
+    int prev_tok = anchor;   /* a target id */
+    for (int j = 0; j < n_pred; ++j) {
+        const double* zj = z + (size_t)j * D;
+        const uint16_t* u = r > 0 ? w1 + (long)prev_tok * r : NULL;
+#pragma omp parallel for schedule(static)
+        for (long i = 0; i < D; ++i) {
+            double m = 0.0;
+            for (int q = 0; q < r; ++q)
+                m += bf16_value(w2[i * (long)r + q]) * bf16_value(u[q]);
+            zp[i] = (float)(zj[i] + m);
+        }
+        const int best = oracle_argmax(zp, D);
+        oracle_topk(zp, D, top_k, idx, cand_val + (size_t)j * top_k);
+        for (int t = 0; t < top_k; ++t)
+            cand[(size_t)j * top_k + t] = (int32_t)d2t[idx[t]];
+        tokens[j] = (int32_t)d2t[best];
+        prev_tok = (int)d2t[best];
+    }
+    free(zp);
+    free(idx);
+    return ORACLE_OK;
+}
+
 /* Confidence of one prediction slot: float(sigma(sum_h x[h] * conf_w[h])). */
 float oracle_conf(const void* hidden, int hidden_is_f32, const uint16_t* conf_w, int L, int H,
                   int i_first_pred, int b, int j)
@@ -275,6 +329,35 @@ int oracle_propose_block(const void* hidden, int hidden_is_f32, const uint16_t* 
     int st = oracle_block_logits(hidden, hidden_is_f32, lm_head, bias, L, H, V, i_first_pred, b, zz);
     if (st == ORACLE_OK)
         st = oracle_block_chain(zz, w1, w2, V, r, anchors[b], n_pred, top_k, tokens, cand, cand_val);
+    if (st == ORACLE_OK) {
+        for (int j = 0; j < n_pred; ++j)
+            conf[j] = conf_w ? oracle_conf(hidden, hidden_is_f32, conf_w, L, H, i_first_pred, b, j)
+                             : 1.0f;
+        *length = conf_w ? oracle_truncate(conf, n_pred, p_min) : n_pred;
+    }
+    if (!z)
+        free(zz);
+    return st;
+}
+
+/* Everything for block b of a reduced draft vocabulary: draft projections
+ * through lm_head [D][H] (no bias; z may be NULL, else [n_pred][D]), the d2t
+ * chain, confidence and truncation as in oracle_propose_block. */
+int oracle_propose_block_d2t(const void* hidden, int hidden_is_f32, const uint16_t* lm_head,
+                             const int64_t* d2t, const uint16_t* w1, const uint16_t* w2,
+                             const uint16_t* conf_w, const int32_t* anchors, int L, int H, int V,
+                             int D, int r, int i_first_pred, int top_k, float p_min, int b,
+                             double* z, int32_t* tokens, int32_t* cand, float* cand_val,
+                             float* conf, int32_t* length)
+{
+    int n_pred = L - i_first_pred;
+    double* zz = z ? z : (double*)malloc(sizeof(double) * (size_t)n_pred * (size_t)D);
+    if (!zz)
+        return ORACLE_ERR;
+    int st = oracle_block_logits(hidden, hidden_is_f32, lm_head, NULL, L, H, D, i_first_pred, b, zz);
+    if (st == ORACLE_OK)
+        st = oracle_block_chain_d2t(zz, w1, w2, d2t, V, D, r, anchors[b], n_pred, top_k, tokens,
+                                    cand, cand_val);
     if (st == ORACLE_OK) {
         for (int j = 0; j < n_pred; ++j)
             conf[j] = conf_w ? oracle_conf(hidden, hidden_is_f32, conf_w, L, H, i_first_pred, b, j)

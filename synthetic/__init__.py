@@ -10,8 +10,10 @@ from .inputs import (  # noqa: F401
     MASK_TOKEN_ID,
     Config,
     Inputs,
+    ReducedInputs,
     bf16_bits_to_f32,
     f32_to_bf16_bits,
     make_inputs,
     make_small,
+    reduce_vocab,
 )

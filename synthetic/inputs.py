@@ -265,3 +265,40 @@ def make_small(B: int, L: int, H: int, V: int, r: int, top_k: int = 1, *,
 def with_config(inp: Inputs, **changes) -> Inputs:
     """Same tensors, different scalar parameters (top_k, p_min, ...)."""
     return replace(inp, cfg=replace(inp.cfg, **changes))
+
+
+@dataclass
+class ReducedInputs:
+    """The same draft in the reduced-vocabulary form: the draft head has D rows,
+    one per entry of d2t (int64 absolute target ids, increasing); markov_w2 has
+    the same D rows; markov_w1 keeps its V target rows (it is indexed by the
+    previous token, a target id); no bias."""
+    cfg: Config                   # sizes of the target vocabulary (cfg.V)
+    hidden: np.ndarray
+    lm_head: np.ndarray           # uint16 bf16 bits [D, H]
+    d2t: np.ndarray               # int64 [D]
+    markov_w1: Optional[np.ndarray]     # uint16 [V, r] or None
+    markov_w2: Optional[np.ndarray]     # uint16 [D, r] or None
+    conf_w: Optional[np.ndarray]
+    anchors: np.ndarray
+
+    @property
+    def D(self) -> int:
+        return int(self.d2t.shape[0])
+
+    @property
+    def hidden_f32(self) -> bool:
+        return self.hidden.dtype == np.float32
+
+
+def reduce_vocab(inp: Inputs) -> ReducedInputs:
+    """The reduced form of an input whose vocabulary was expanded: d2t lists the
+    reachable target ids, and the head and markov_w2 keep only their rows (a row
+    selection; the expanded form has zero rows and a -1e9 bias elsewhere)."""
+    if inp.reachable is None:
+        raise ValueError("the input has no reduced vocabulary")
+    d2t = np.ascontiguousarray(inp.reachable, dtype=np.int64)
+    w2 = None if inp.markov_w2 is None else np.ascontiguousarray(inp.markov_w2[d2t])
+    return ReducedInputs(cfg=inp.cfg, hidden=inp.hidden, lm_head=np.ascontiguousarray(inp.lm_head[d2t]),
+                         d2t=d2t, markov_w1=inp.markov_w1, markov_w2=w2, conf_w=inp.conf_w,
+                         anchors=inp.anchors)

@@ -16,7 +16,7 @@ from dataclasses import replace
 
 import numpy as np
 
-from synthetic import bf16_bits_to_f32, f32_to_bf16_bits, make_small
+from synthetic import ReducedInputs, bf16_bits_to_f32, f32_to_bf16_bits, make_small, reduce_vocab
 from synthetic.inputs import BONUS_ANCHOR, Config, Inputs
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -412,6 +412,48 @@ def pin_no_conf_head_keeps_full_block(orc):
     out = orc.propose(replace(inp, cfg=replace(inp.cfg, p_min=0.9)))
     assert out["lengths"].tolist() == [5, 5]
     assert np.all(out["conf"] == 1.0)
+
+
+def _d2t_cases():
+    from synthetic.inputs import BONUS_ANCHOR
+    return [
+        make_small(3, 5, 64, 700, 16, top_k=3, reachable=90, conf=True, p_min=0.45, seed=31),
+        make_small(2, 6, 32, 300, 0, top_k=2, reachable=40, seed=32),
+        make_small(2, 5, 48, 257, 8, top_k=4, reachable=4, layout=BONUS_ANCHOR, conf=True,
+                   p_min=0.5, conf_trend=True, seed=33),
+    ]
+
+
+def pin_d2t_equals_expanded_form(orc):
+    """The run-time d2t scatter (llama.cpp PR #26275, rework commit message)
+    and the expanded form it replaces (first commit message: lm_head and
+    markov_w2 rows placed at their target ids, zero rows and a -1e9 bias
+    elsewhere) give the same tokens, candidates, scores, confidences and
+    cuts; the draft projections are the expanded ones at the d2t columns."""
+    for inp in _d2t_cases():
+        red = reduce_vocab(inp)
+        assert not np.array_equal(red.d2t, np.arange(red.D))   # a real remap
+        for b in range(inp.cfg.B):
+            e = orc.propose_block(inp, b)
+            d = orc.propose_block_d2t(red, b)
+            for key in ("tokens", "candidates", "cand_logits", "conf"):
+                assert np.array_equal(e[key], d[key]), key
+            assert e["length"] == d["length"]
+            assert np.array_equal(e["logits"][:, red.d2t], d["logits"])
+            assert set(d["candidates"].ravel().tolist()) <= set(red.d2t.tolist())
+
+
+def pin_d2t_identity_is_plain(orc):
+    """With D = V and d2t the identity, the reduced form is the plain step."""
+    inp = make_small(2, 4, 32, 200, 8, top_k=3, conf=True, p_min=0.4, seed=34)
+    red = ReducedInputs(cfg=inp.cfg, hidden=inp.hidden, lm_head=inp.lm_head,
+                        d2t=np.arange(inp.cfg.V, dtype=np.int64), markov_w1=inp.markov_w1,
+                        markov_w2=inp.markov_w2, conf_w=inp.conf_w, anchors=inp.anchors)
+    for b in range(inp.cfg.B):
+        e = orc.propose_block(inp, b)
+        d = orc.propose_block_d2t(red, b)
+        for key in ("logits", "tokens", "candidates", "cand_logits", "conf"):
+            assert np.array_equal(e[key], d[key]), key
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -103,6 +103,36 @@ def test_propose_rejects_workspace(lib):
     assert propose(lib, ws=P + 64) == dsp.ERR_WORKSPACE
 
 
+def propose_d2t(lib, **kw):
+    a = dict(hidden=P, hidden_dtype=0, lm_head=P, d2t=P, w1=P, w2=P, conf_w=P, anchors=P,
+             B=2, L=4, H=64, V=4096, D=512, r=8, layout=0, top_k=2, p_min=0.5, logits=P, ws=P,
+             ws_bytes=1 << 30, tokens=P, cand=P, cand_logits=P, conf=P, lengths=P, stream=None)
+    a.update(kw)
+    return lib.dspark_propose_d2t(a["hidden"], a["hidden_dtype"], a["lm_head"], a["d2t"], a["w1"],
+                                  a["w2"], a["conf_w"], a["anchors"], a["B"], a["L"], a["H"], a["V"],
+                                  a["D"], a["r"], a["layout"], a["top_k"], ctypes.c_float(a["p_min"]),
+                                  a["logits"], a["ws"], a["ws_bytes"], a["tokens"], a["cand"],
+                                  a["cand_logits"], a["conf"], a["lengths"], a["stream"])
+
+
+INVALID_D2T = [dict(D=0), dict(V=0), dict(D=4097), dict(d2t=None), dict(D=3, top_k=4),
+               dict(lm_head=None), dict(w2=None), dict(layout=3), dict(p_min=float("nan"))]
+
+
+@pytest.mark.parametrize("kw", INVALID_D2T, ids=[",".join(f"{k}={v}" for k, v in d.items()) for d in INVALID_D2T])
+def test_propose_d2t_rejects_invalid(lib, kw):
+    assert propose_d2t(lib, **kw) == dsp.ERR_INVALID_ARG
+
+
+def test_propose_d2t_rejects_unsupported_and_workspace(lib):
+    assert propose_d2t(lib, d2t=P + 4) == dsp.ERR_UNSUPPORTED     # int64 table misaligned
+    assert propose_d2t(lib, H=60) == dsp.ERR_UNSUPPORTED
+    # the workspace is sized for the D draft columns
+    need = lib.dspark_workspace_bytes(2, 4, 512, 2, 0)
+    assert propose_d2t(lib, ws_bytes=need - 1) == dsp.ERR_WORKSPACE
+    assert propose_d2t(lib, ws=None) == dsp.ERR_WORKSPACE
+
+
 def test_r0_needs_null_markov(lib):
     # r == 0 is valid only with both Markov pointers NULL; r > 0 needs both
     assert propose(lib, r=0, w1=P, w2=None) == dsp.ERR_INVALID_ARG

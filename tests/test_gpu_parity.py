@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 from oracle.check import check
-from synthetic import CONFIGS, make_inputs, make_small
+from synthetic import CONFIGS, make_inputs, make_small, reduce_vocab
 from synthetic.inputs import BONUS_ANCHOR
 
 pytestmark = pytest.mark.gpu
@@ -160,6 +160,67 @@ def test_workspace_reuse_across_shapes(dev, orc):
     run_propose(big, out=out)
     g = to_host(run_propose(small, out=out))
     check(orc, small, g)
+
+
+# ---- reduced draft vocabulary (d2t table) ------------------------------------
+
+D2T_SMALL = {
+    "d2t_k4_conf": lambda: make_small(5, 7, 136, 3000, 16, top_k=4, layout=BONUS_ANCHOR,
+                                      reachable=300, conf=True, p_min=0.5, conf_trend=True, seed=41),
+    "d2t_top1_r64": lambda: make_small(3, 9, 64, 5000, 64, top_k=1, reachable=1031, seed=42),
+    "d2t_ragged_D": lambda: make_small(37, 6, 128, 2000, 8, top_k=2, reachable=333, seed=43),
+    "d2t_topk_equals_D": lambda: make_small(2, 4, 32, 700, 8, top_k=5, reachable=5, seed=44),
+}
+
+
+def _same_outputs(a: dict, b: dict):
+    for k in ("tokens", "candidates", "cand_logits", "conf", "lengths"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("name", sorted(D2T_SMALL))
+def test_d2t_equals_expanded_form(dev, orc, name):
+    """The d2t path (projection and chain over the D draft ids) against the
+    expanded form through dspark_propose: bit for bit on every output, the
+    draft projections equal to the expanded ones at the d2t columns; and the
+    re-conditioning checker against the oracle."""
+    from devutil import run_propose_d2t, scatter_logits, to_host
+    inp = D2T_SMALL[name]()
+    red = reduce_vocab(inp)
+    _say(f"[d2t] {name}: {inp.cfg} D={red.D}")
+    e = _gpu(inp)
+    g = to_host(run_propose_d2t(red))
+    _same_outputs(e, g)
+    assert np.array_equal(e["logits"][:, red.d2t], g["logits"])
+    g["logits"] = scatter_logits(g["logits"], red.d2t, inp.cfg.V)
+    check(orc, inp, g)
+
+
+def test_d2t_bad_entry_raises_flag_without_fault(dev):
+    import dspark_block_drafter_amd as dsp
+    from devutil import run_propose_d2t
+    red = reduce_vocab(make_small(2, 4, 32, 500, 8, top_k=2, reachable=50, seed=45))
+    bad = replace(red, d2t=np.full(red.D, 10_000_000, dtype=np.int64))
+    res = run_propose_d2t(bad)
+    assert dsp.read_flags(res) & dsp.FLAG_BAD_D2T
+    res = run_propose_d2t(red)
+    assert dsp.read_flags(res) == 0
+
+
+def test_d2t_full_size_gemma(dev, orc):
+    """The Gemma-4-26B-A4B workload in its reduced form (D = 32768 of
+    V = 262144): every block equal to the expanded form, sampled blocks against
+    the oracle."""
+    from devutil import run_propose_d2t, scatter_logits, to_host
+    inp = make_inputs(CONFIGS["gemma4_26b_a4b"])
+    red = reduce_vocab(inp)
+    e = _gpu(inp)
+    g = to_host(run_propose_d2t(red))
+    _say(f"[d2t] gemma: GPU done, D={red.D}")
+    _same_outputs(e, g)
+    assert np.array_equal(e["logits"][:, red.d2t], g["logits"])
+    g["logits"] = scatter_logits(g["logits"], red.d2t, inp.cfg.V)
+    check(orc, inp, g, blocks=[0, 3])
 
 
 # ---- full-size workloads, sampled blocks ------------------------------------

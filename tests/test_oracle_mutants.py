@@ -36,6 +36,14 @@ MUTANTS = {
                         "load_hidden_row(hidden, hidden_is_f32, (long)b * L + j, H, x);"),
     "truncate_short": ("            return j;\n    return n_pred;", "            return j;\n    return n_pred - 1;"),
     "markov_rank_short": ("for (int k = 0; k < r; ++k)", "for (int k = 1; k < r; ++k)"),
+    "d2t_prev_is_draft_id": ("prev_tok = (int)d2t[best];", "prev_tok = best;"),
+    "d2t_prev0_not_anchor": ("int prev_tok = anchor;", "int prev_tok = 0;"),
+    "d2t_token_unmapped": ("tokens[j] = (int32_t)d2t[best];", "tokens[j] = best;"),
+    "d2t_candidates_unmapped": ("cand[(size_t)j * top_k + t] = (int32_t)d2t[idx[t]];",
+                                "cand[(size_t)j * top_k + t] = idx[t];"),
+    "d2t_markov_dropped": ("zp[i] = (float)(zj[i] + m);", "zp[i] = (float)(zj[i]);"),
+    "d2t_w1_by_draft_row": ("const uint16_t* u = r > 0 ? w1 + (long)prev_tok * r : NULL;",
+                            "const uint16_t* u = r > 0 ? w1 + (long)(prev_tok % D) * r : NULL;"),
     "hidden_f32_truncated": ("x[h] = bf16_value(oracle_bf16_round(p[h]));",
                              "x[h] = bf16_value((uint16_t)(*(const uint32_t*)&p[h] >> 16));"),
 }
