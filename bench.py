@@ -185,6 +185,23 @@ def main() -> int:
     chain_ms = (ms - gemm_ms) if args.d2t else sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     log(f"lm_head GEMM {gemm_ms * 1e3:.1f} us, chain+finalize {chain_ms * 1e3:.1f} us")
 
+    # Greedy lattice verification of the step's proposal (dspark_verify), with
+    # the target taken equal to the drafted chain: every submitted slot is
+    # walked, the longest walk the data allows.
+    acc_buf = torch.empty((cfg.B,), dtype=torch.int32, device="cuda:0")
+    tot_buf = torch.empty((2,), dtype=torch.int32, device="cuda:0")
+    target = out.tokens.clone()
+    v0, v1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    v0.record(stream)
+    for _ in range(args.steps):
+        dsp.verify(out.candidates, out.lengths, target, lattice=True, accepted=acc_buf,
+                   totals=tot_buf, stream=stream)
+    v1.record(stream)
+    torch.cuda.synchronize()
+    verify_us = v0.elapsed_time(v1) / args.steps * 1e3
+    walked = tot_buf.cpu().tolist()
+    log(f"lattice verify {verify_us:.1f} us per call ({walked[0]} of {walked[1]} submitted slots walked)")
+
     M, H, V, r, B, n = cfg.B * cfg.n_pred, cfg.H, N, cfg.r, cfg.B, cfg.n_pred
     flops = 2.0 * M * H * V
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
@@ -227,6 +244,8 @@ def main() -> int:
                            "bytes": chain_bytes, "kernels": "chain_init + chain_step x n_pred + finalize",
                            "us": chain_ms * 1e3},
         "wall_ms_per_step": 1e3 * wall / args.steps,
+        "verify": {"kernel": "verify_walk", "us": verify_us, "lattice": True,
+                   "submitted_slots": walked[1]},
     }
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_blocks} blocks")

@@ -37,7 +37,7 @@ MAX_TOP_K = 16
 MAX_RANK = 256
 
 EXPORTS = ("dspark_workspace_bytes", "dspark_propose", "dspark_logits", "dspark_chain",
-           "dspark_propose_d2t", "dspark_read_flags", "dspark_status_string")
+           "dspark_propose_d2t", "dspark_verify", "dspark_read_flags", "dspark_status_string")
 
 
 class DsparkError(RuntimeError):
@@ -78,6 +78,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                        _i, _i, _i, _i, _i, _i, _i, _i, _f,
                                        _vp, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.dspark_propose_d2t.restype = _i
+    lib.dspark_verify.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp]
+    lib.dspark_verify.restype = _i
     lib.dspark_read_flags.argtypes = [_vp, ctypes.POINTER(ctypes.c_uint32), _vp]
     lib.dspark_read_flags.restype = _i
     lib.dspark_status_string.argtypes = [_i]
@@ -271,6 +273,28 @@ def chain(logits_in, markov_w1, markov_w2, anchors, *, B, L, layout="anchor_firs
     if st != OK:
         raise DsparkError(st, "dspark_chain")
     return out
+
+
+def verify(candidates, lengths, target, *, lattice: bool = False, accepted=None, totals=None,
+           stream=None):
+    """Run dspark_verify; returns (accepted [B], totals [2]) as device int32 tensors."""
+    torch = _torch()
+    lib = load_library()
+    B, n, k = candidates.shape
+    _check_dev("candidates", candidates, torch.int32)
+    _check_dev("lengths", lengths, torch.int32, (B,))
+    _check_dev("target", target, torch.int32, (B, n))
+    if accepted is None:
+        accepted = torch.empty((B,), dtype=torch.int32, device=candidates.device)
+    if totals is None:
+        totals = torch.empty((2,), dtype=torch.int32, device=candidates.device)
+    _check_dev("accepted", accepted, torch.int32, (B,))
+    _check_dev("totals", totals, torch.int32, (2,))
+    st = lib.dspark_verify(_ptr(candidates), _ptr(lengths), _ptr(target), B, n, k, int(bool(lattice)),
+                           _ptr(accepted), _ptr(totals), _stream(candidates, stream))
+    if st != OK:
+        raise DsparkError(st, "dspark_verify")
+    return accepted, totals
 
 
 def read_flags(out: Outputs, stream=None) -> int:

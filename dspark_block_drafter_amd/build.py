@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libdspark.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["lmhead_gemm.hip", "markov_chain.hip", "dspark_api.hip"]
+SOURCES = ["lmhead_gemm.hip", "markov_chain.hip", "lattice_verify.hip", "dspark_api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

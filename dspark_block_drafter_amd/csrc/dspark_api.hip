@@ -246,6 +246,26 @@ int dspark_propose_d2t(const void* hidden, int hidden_dtype, const uint16_t* lm_
                      cand_logits, conf, lengths, static_cast<hipStream_t>(stream));
 }
 
+int dspark_verify(const int32_t* candidates, const int32_t* lengths, const int32_t* target, int B,
+                  int n_pred, int top_k, int lattice, int32_t* accepted, int32_t* totals,
+                  void* stream) {
+    if (B <= 0 || n_pred <= 0 || top_k < 1 || top_k > DSPARK_MAX_TOP_K) return DSPARK_ERR_INVALID_ARG;
+    if (lattice != 0 && lattice != 1) return DSPARK_ERR_INVALID_ARG;
+    if (!candidates || !lengths || !target || !accepted || !totals) return DSPARK_ERR_INVALID_ARG;
+    if ((long)B * n_pred * top_k > 0x7fffffffL) return DSPARK_ERR_UNSUPPORTED;
+    VerifyArgs v;
+    v.candidates = candidates;
+    v.lengths = lengths;
+    v.target = target;
+    v.accepted = accepted;
+    v.totals = totals;
+    v.B = B;
+    v.n_pred = n_pred;
+    v.top_k = top_k;
+    v.width = lattice ? top_k : 1;
+    return hip_status(launch_verify(v, static_cast<hipStream_t>(stream)));
+}
+
 int dspark_read_flags(const void* workspace, uint32_t* flags, void* stream) {
     if (!workspace || !flags) return DSPARK_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);

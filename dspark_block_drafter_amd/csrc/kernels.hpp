@@ -87,4 +87,16 @@ struct FinalArgs {
 };
 hipError_t launch_finalize(const FinalArgs& a, hipStream_t stream);
 
+// ---- greedy verification ---------------------------------------------------------
+struct VerifyArgs {
+    const int32_t* candidates; // [B, n_pred, top_k]
+    const int32_t* lengths;    // [B], clamped to [0, n_pred]
+    const int32_t* target;     // [B, n_pred]: the target's greedy token per slot
+    int32_t* accepted;         // [B]
+    int32_t* totals;           // [2]: sum of accepted, sum of the clamped lengths
+    int B, n_pred, top_k;
+    int width;                 // candidates checked per slot: 1 (the chain) or top_k (lattice)
+};
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
+
 }  // namespace dspark

@@ -211,6 +211,33 @@ int dspark_propose_d2t(const void* hidden, int hidden_dtype, const uint16_t* lm_
                        void* stream);
 
 /*
+ * Greedy verification of a proposal against the target's tokens: the target
+ * keeps the longest drafted prefix it would have produced itself, so greedy
+ * speculation stays lossless (llama.cpp commit 6fed9f6 "spec: add DSpark
+ * speculative decoding", the in-graph chain item). With lattice = 0 slot j of
+ * block b is accepted when target[b][j] == candidates[b][j][0] (the greedy
+ * chain); with lattice = 1 when target[b][j] is any of the slot's top_k
+ * candidates, the greedy walk of the candidate lattice (onnxruntime-genai PR
+ * #2490 "Export DSpark block drafters for Qwen 3.5 and 3.8", DFlash 2 and
+ * DSpark commit messages). The walk of block b stops at the first slot that
+ * is not accepted and at lengths[b] (clamped to [0, n_pred]): a truncated
+ * block submits only its surviving slots.
+ *
+ *   candidates    DEVICE int32 [B, n_pred, top_k], as dspark_propose writes it.
+ *   lengths       DEVICE int32 [B], as dspark_propose writes it.
+ *   target        DEVICE int32 [B, n_pred]: the target's greedy token at each
+ *                 slot, given the slots before it.
+ *   accepted      DEVICE int32 [B] output: accepted slots per block.
+ *   totals        DEVICE int32 [2] output: sum of accepted, sum of the clamped
+ *                 lengths (the acceptance rate is their ratio).
+ *   B, n_pred, top_k  sizes, 1 <= top_k <= DSPARK_MAX_TOP_K; lattice 0 or 1.
+ * Needs no workspace. Returns a dspark_status.
+ */
+int dspark_verify(const int32_t* candidates, const int32_t* lengths, const int32_t* target, int B,
+                  int n_pred, int top_k, int lattice, int32_t* accepted, int32_t* totals,
+                  void* stream);
+
+/*
  * Copies the flags word of `workspace` (written by the last dspark_propose /
  * dspark_propose_d2t / dspark_chain on it) to *flags after `stream` has drained; this call does
  * synchronise the stream. Returns a dspark_status.

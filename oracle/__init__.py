@@ -83,15 +83,20 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
                                              _i, _i, _i, _i, _i, _i, _i, ctypes.c_float, _i,
                                              _f64p, _i32p, _i32p, _f32p, _f32p, _i32p]
     lib.oracle_propose_block_d2t.restype = _i
+    lib.oracle_verify.argtypes = [_i32p, _i32p, _i32p, _i, _i, _i, _i, _i32p, _i64p]
+    lib.oracle_verify.restype = _i
     return lib
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load liboracle.so, compiling it first if it has not been built."""
+    """Load liboracle.so, compiling it first if it is missing or older than its source."""
     global _LIB
     if path == LIB_PATH and _LIB is not None:
         return _LIB
-    if not os.path.exists(path):
+    if path == LIB_PATH and (not os.path.exists(path)
+                             or os.path.getmtime(path) < os.path.getmtime(SRC_PATH)):
+        build(out=path)
+    elif not os.path.exists(path):
         build(out=path)
     lib = _declare(ctypes.CDLL(path))
     if path == LIB_PATH:
@@ -211,6 +216,21 @@ class Oracle:
             raise ValueError("oracle_propose_block rejected its arguments")
         return {"logits": z, "tokens": tokens, "candidates": cand, "cand_logits": cval,
                 "conf": conf, "length": int(length[0])}
+
+    def verify(self, candidates: np.ndarray, lengths: np.ndarray, target: np.ndarray,
+               lattice: bool = False):
+        """Accepted slots per block and (sum accepted, sum clamped lengths)."""
+        cand = np.ascontiguousarray(candidates, dtype=np.int32)
+        B, n, k = cand.shape
+        lengths = np.ascontiguousarray(lengths, dtype=np.int32)
+        target = np.ascontiguousarray(target, dtype=np.int32)
+        acc = np.empty(B, dtype=np.int32)
+        tot = np.zeros(2, dtype=np.int64)
+        st = self.lib.oracle_verify(_p(cand, _i32p), _p(lengths, _i32p), _p(target, _i32p), B, n, k,
+                                    k if lattice else 1, _p(acc, _i32p), _p(tot, _i64p))
+        if st != 0:
+            raise ValueError("oracle_verify rejected its arguments")
+        return acc, (int(tot[0]), int(tot[1]))
 
     def propose_block_d2t(self, red, b: int, keep_logits: bool = True) -> dict:
         """Block b of a reduced-vocabulary input (``synthetic.ReducedInputs``)."""

@@ -39,6 +39,14 @@
  * chosen draft ids are reported as target ids. Every target id off the table
  * has no score, so it can never be chosen.
  *
+ * Verification: greedy speculation is lossless because the target keeps only
+ * the longest drafted prefix it would have produced itself (llama.cpp commit
+ * 6fed9f6, the in-graph chain item: verification unchanged from DFlash); with
+ * a candidate lattice the engine walks it greedily, accepting a slot when the
+ * target's token is among the slot's candidates (onnxruntime-genai PR #2490,
+ * DFlash 2 and DSpark commit messages). A block submits only its
+ * confidence-truncated slots.
+ *
  * Block layouts: anchor-first (every slot predicts; i_first_pred = 0) and the
  * 1+N bonus-anchor layout (slot 0 holds the bonus token and is never read;
  * i_first_pred = 1) (llama.cpp PR #26275, first commit message and
@@ -367,4 +375,39 @@ int oracle_propose_block_d2t(const void* hidden, int hidden_is_f32, const uint16
     if (!z)
         free(zz);
     return st;
+}
+
+/* Greedy verification of B blocks: block b accepts slot j while target[b][j]
+ * is one of the first `width` candidates of the slot (width 1: the chain
+ * token; width top_k: the lattice), over at most min(max(lengths[b], 0),
+ * n_pred) slots. totals[0] = sum of accepted, totals[1] = sum of the clamped
+ * lengths. */
+int oracle_verify(const int32_t* cand, const int32_t* lengths, const int32_t* target, int B,
+                  int n_pred, int top_k, int width, int32_t* accepted, int64_t* totals)
+{
+    if (B < 1 || n_pred < 1 || top_k < 1 || width < 1 || width > top_k)
+        return ORACLE_ERR;
+    totals[0] = 0;
+    totals[1] = 0;
+    for (int b = 0; b < B; ++b) {
+        int len = lengths[b] < 0 ? 0 : lengths[b];
+        if (len > n_pred)
+            len = n_pred;
+        int m = 0;
+        while (m < len) {
+            const int32_t* c = cand + ((size_t)b * n_pred + m) * top_k;
+            const int32_t t = target[(size_t)b * n_pred + m];
+            int found = 0;
+            for (int i = 0; i < width; ++i)
+                if (c[i] == t)
+                    found = 1;
+            if (!found)
+                break;
+            ++m;
+        }
+        accepted[b] = m;
+        totals[0] += m;
+        totals[1] += len;
+    }
+    return ORACLE_OK;
 }

@@ -456,4 +456,51 @@ def pin_d2t_identity_is_plain(orc):
             assert np.array_equal(e[key], d[key]), key
 
 
+def pin_verify_hand_example(orc):
+    """Greedy verification worked by hand. Candidates [B=3, n=4, k=2]:
+    block 0 drafts 5 6 7 8 (runners-up 1 2 3 4), length 4, target 5 6 3 8:
+    the chain stops at slot 2 (3 is not the draft 7), the lattice takes the
+    runner-up 3 and then 8: 2 and 4. Block 1, length 2 (truncated), target
+    equal to the draft everywhere: 2 for both (the cut ends the walk).
+    Block 2, target 9 at slot 0: 0 for both."""
+    cand = np.array([[[5, 1], [6, 2], [7, 3], [8, 4]],
+                     [[1, 2], [3, 4], [5, 6], [7, 8]],
+                     [[4, 5], [6, 7], [8, 9], [1, 2]]], dtype=np.int32)
+    lengths = np.array([4, 2, 4], dtype=np.int32)
+    target = np.array([[5, 6, 3, 8], [1, 3, 5, 7], [9, 6, 8, 1]], dtype=np.int32)
+    acc, tot = orc.verify(cand, lengths, target, lattice=False)
+    assert acc.tolist() == [2, 2, 0] and tot == (4, 10)
+    acc, tot = orc.verify(cand, lengths, target, lattice=True)
+    assert acc.tolist() == [4, 2, 0] and tot == (6, 10)
+
+
+def pin_verify_bruteforce(orc):
+    """Random small lattices against the definition written as a maximum: the
+    largest m <= clamped length such that every slot below m holds the target
+    among its first w candidates. Also: target equal to the chain accepts the
+    whole submitted block, and the lattice never accepts less than the chain."""
+    rng = np.random.default_rng(7)
+    for _ in range(40):
+        B, n, k = int(rng.integers(1, 6)), int(rng.integers(1, 7)), int(rng.integers(1, 5))
+        cand = rng.integers(0, 5, size=(B, n, k)).astype(np.int32)
+        lengths = rng.integers(-1, n + 2, size=B).astype(np.int32)
+        target = rng.integers(0, 5, size=(B, n)).astype(np.int32)
+        for lattice in (False, True):
+            w = k if lattice else 1
+            acc, tot = orc.verify(cand, lengths, target, lattice=lattice)
+            want = []
+            for b in range(B):
+                cap = min(max(int(lengths[b]), 0), n)
+                ok = [m for m in range(cap + 1)
+                      if all(target[b, j] in cand[b, j, :w].tolist() for j in range(m))]
+                want.append(max(ok))
+            assert acc.tolist() == want
+            assert tot == (sum(want), sum(min(max(int(l), 0), n) for l in lengths))
+        chain_acc, _ = orc.verify(cand, lengths, target, lattice=False)
+        lat_acc, _ = orc.verify(cand, lengths, target, lattice=True)
+        assert np.all(lat_acc >= chain_acc)
+        acc, _ = orc.verify(cand, lengths, cand[:, :, 0], lattice=False)
+        assert acc.tolist() == [min(max(int(l), 0), n) for l in lengths]
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

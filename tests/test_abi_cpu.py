@@ -133,6 +133,18 @@ def test_propose_d2t_rejects_unsupported_and_workspace(lib):
     assert propose_d2t(lib, ws=None) == dsp.ERR_WORKSPACE
 
 
+def test_verify_rejects_invalid(lib):
+    def v(**kw):
+        a = dict(cand=P, lengths=P, target=P, B=4, n=8, k=2, lattice=1, acc=P, tot=P)
+        a.update(kw)
+        return lib.dspark_verify(a["cand"], a["lengths"], a["target"], a["B"], a["n"], a["k"],
+                                 a["lattice"], a["acc"], a["tot"], None)
+    for kw in (dict(B=0), dict(n=0), dict(k=0), dict(k=17), dict(lattice=2), dict(cand=None),
+               dict(lengths=None), dict(target=None), dict(acc=None), dict(tot=None)):
+        assert v(**kw) == dsp.ERR_INVALID_ARG, kw
+    assert v(B=1 << 20, n=1 << 8, k=16) == dsp.ERR_UNSUPPORTED
+
+
 def test_r0_needs_null_markov(lib):
     # r == 0 is valid only with both Markov pointers NULL; r > 0 needs both
     assert propose(lib, r=0, w1=P, w2=None) == dsp.ERR_INVALID_ARG

@@ -223,6 +223,53 @@ def test_d2t_full_size_gemma(dev, orc):
     check(orc, inp, g, blocks=[0, 3])
 
 
+# ---- greedy verification of the lattice -----------------------------------------
+
+def _verify_tables(B, n, k, vocab, seed, p_hit=0.8):
+    """Seeded candidate tables and targets: a target equals the chain token
+    with probability p_hit, else the runner-up or a random id."""
+    rng = np.random.default_rng(seed)
+    cand = rng.integers(0, vocab, size=(B, n, k)).astype(np.int32)
+    lengths = rng.integers(-1, n + 2, size=B).astype(np.int32)
+    u = rng.random((B, n))
+    target = np.where(u < p_hit, cand[:, :, 0],
+                      np.where(u < (1 + p_hit) / 2, cand[:, :, min(1, k - 1)],
+                               rng.integers(0, vocab, size=(B, n)))).astype(np.int32)
+    return cand, lengths, target
+
+
+@pytest.mark.parametrize("shape", [(3, 5, 1), (64, 16, 4), (257, 7, 16), (100_003, 6, 2)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_verify_against_oracle(dev, orc, shape):
+    import torch
+
+    import dspark_block_drafter_amd as dsp
+    B, n, k = shape
+    cand, lengths, target = _verify_tables(B, n, k, vocab=50, seed=B + n + k)
+    t = lambda a: torch.from_numpy(a).to(dev)
+    for lattice in (False, True):
+        acc, tot = dsp.verify(t(cand), t(lengths), t(target), lattice=lattice)
+        torch.cuda.synchronize()
+        want_acc, want_tot = orc.verify(cand, lengths, target, lattice=lattice)
+        assert np.array_equal(acc.cpu().numpy(), want_acc)
+        assert tuple(tot.cpu().numpy().tolist()) == want_tot
+
+
+def test_verify_own_chain_accepts_whole_blocks(dev):
+    """Verified against its own greedy chain, a proposal keeps every submitted
+    slot."""
+    import torch
+
+    import dspark_block_drafter_amd as dsp
+    inp = make_small(9, 6, 64, 3000, 16, top_k=3, conf=True, p_min=0.45, seed=46)
+    res = _gpu(inp)
+    dv = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    acc, tot = dsp.verify(dv(res["candidates"]), dv(res["lengths"]), dv(res["tokens"]))
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), res["lengths"])
+    assert tot.cpu().numpy().tolist() == [int(res["lengths"].sum())] * 2
+
+
 # ---- full-size workloads, sampled blocks ------------------------------------
 
 FULL = {

@@ -44,6 +44,12 @@ MUTANTS = {
     "d2t_markov_dropped": ("zp[i] = (float)(zj[i] + m);", "zp[i] = (float)(zj[i]);"),
     "d2t_w1_by_draft_row": ("const uint16_t* u = r > 0 ? w1 + (long)prev_tok * r : NULL;",
                             "const uint16_t* u = r > 0 ? w1 + (long)(prev_tok % D) * r : NULL;"),
+    "verify_no_length_cap": ("        while (m < len) {", "        while (m < n_pred) {"),
+    "verify_lattice_first_only": ("            for (int i = 0; i < width; ++i)\n                if (c[i] == t)",
+                                  "            for (int i = 0; i < 1; ++i)\n                if (c[i] == t)"),
+    "verify_counts_all_matches": ("            if (!found)\n                break;\n            ++m;",
+                                  "            if (!found) {\n                ++m;\n                continue;\n            }\n            ++m;"),
+    "verify_total_unclamped": ("        totals[1] += len;", "        totals[1] += lengths[b];"),
     "hidden_f32_truncated": ("x[h] = bf16_value(oracle_bf16_round(p[h]));",
                              "x[h] = bf16_value((uint16_t)(*(const uint32_t*)&p[h] >> 16));"),
 }
