@@ -96,6 +96,9 @@ def main() -> int:
     ap.add_argument("--workload", default="qwen38_27b_throughput")
     ap.add_argument("--cpu-blocks", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--adaptive", action="store_true",
+                    help="run dspark_propose_adaptive (confidence gate before the chain, "
+                         "the workload's p_min for every block); value counts submitted slots")
     ap.add_argument("--d2t", action="store_true",
                     help="run the workload's reduced-vocabulary form (dspark_propose_d2t)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -136,6 +139,20 @@ def main() -> int:
             dsp.propose_d2t(d["hidden"], d["lm_head"], d["d2t"], d["markov_w1"], d["markov_w2"],
                             d["anchors"], vocab=cfg.V, layout=cfg.layout, top_k=cfg.top_k,
                             p_min=cfg.p_min, conf_w=d["conf_w"], out=out, stream=stream)
+    elif args.adaptive:
+        if inp.conf_w is None:
+            print(f"--adaptive needs a confidence head; {cfg.name} has none", file=sys.stderr)
+            return 2
+        d = to_device(inp)
+        N = cfg.V
+        out = dsp.Outputs(cfg.B, cfg.L, cfg.V, cfg.top_k, cfg.layout, "cuda:0")
+        p_min_b = torch.full((cfg.B,), float(cfg.p_min), dtype=torch.float32, device="cuda:0")
+
+        def step():
+            dsp.propose_adaptive(d["hidden"], d["lm_head"], d["markov_w1"], d["markov_w2"],
+                                 d["anchors"], d["conf_w"], p_min_b, layout=cfg.layout,
+                                 top_k=cfg.top_k, lm_head_bias=d["lm_head_bias"], out=out,
+                                 stream=stream)
     else:
         d = to_device(inp)
         N = cfg.V
@@ -164,10 +181,13 @@ def main() -> int:
     ms = ev0.elapsed_time(ev1) / args.steps
     log(f"timed {args.steps} steps: {ms:.3f} ms/step (events), {1e3 * wall / args.steps:.3f} ms/step (wall)")
     assert dsp.read_flags(out) == 0
+    submitted = int(out.lengths.sum().item())
+    if args.adaptive:
+        log(f"adaptive gate: {submitted} of {cfg.drafted_tokens} slots submitted per step")
 
     # Per-kernel split: the same projection through dspark_logits, then the
-    # chain through dspark_chain (the d2t form has no separate chain entry:
-    # its chain time is the step minus the projection).
+    # chain through dspark_chain (the d2t and adaptive forms have no separate
+    # chain entry: their chain time is the step minus the projection).
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for e in evs:
         e[0].record(stream)
@@ -175,14 +195,15 @@ def main() -> int:
                    lm_head_bias=None if args.d2t else d["lm_head_bias"], out=out.logits,
                    stream=stream)
         e[1].record(stream)
-        if not args.d2t:
+        if not (args.d2t or args.adaptive):
             dsp.chain(out.logits, d["markov_w1"], d["markov_w2"], d["anchors"], B=cfg.B, L=cfg.L,
                       layout=cfg.layout, top_k=cfg.top_k, p_min=cfg.p_min, hidden=d["hidden"],
                       conf_w=d["conf_w"], out=out, stream=stream)
         e[2].record(stream)
     torch.cuda.synchronize()
     gemm_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    chain_ms = (ms - gemm_ms) if args.d2t else sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    chain_ms = ((ms - gemm_ms) if (args.d2t or args.adaptive)
+                else sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps)
     log(f"lm_head GEMM {gemm_ms * 1e3:.1f} us, chain+finalize {chain_ms * 1e3:.1f} us")
 
     # Greedy lattice verification of the step's proposal (dspark_verify), with
@@ -221,7 +242,7 @@ def main() -> int:
 
     res = {
         "metric": METRIC,
-        "value": cfg.drafted_tokens / (ms * 1e-3),
+        "value": (submitted if args.adaptive else cfg.drafted_tokens) / (ms * 1e-3),
         "unit": "drafted tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -235,7 +256,9 @@ def main() -> int:
         "config": {"workload": cfg.name, "B": cfg.B, "L": cfg.L, "H": H, "V": cfg.V, "r": r,
                    "top_k": cfg.top_k, "p_min": cfg.p_min, "layout": cfg.layout,
                    "drafted_tokens_per_step": cfg.drafted_tokens,
-                   **({"d2t_draft_vocab": N} if args.d2t else {})},
+                   **({"d2t_draft_vocab": N} if args.d2t else {}),
+                   **({"adaptive": True, "counted": "submitted slots (sum of lengths)",
+                       "submitted_per_step": submitted} if args.adaptive else {})},
         "roofline": {**gemm_roof,
                      "traffic": None if args.d2t else measured_traffic(cfg.name),
                      "kernel": "lmhead_gemm", "us": gemm_ms * 1e3},

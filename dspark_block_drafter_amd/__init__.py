@@ -37,7 +37,8 @@ MAX_TOP_K = 16
 MAX_RANK = 256
 
 EXPORTS = ("dspark_workspace_bytes", "dspark_propose", "dspark_logits", "dspark_chain",
-           "dspark_propose_d2t", "dspark_verify", "dspark_read_flags", "dspark_status_string")
+           "dspark_propose_d2t", "dspark_propose_adaptive", "dspark_verify", "dspark_read_flags",
+           "dspark_status_string")
 
 
 class DsparkError(RuntimeError):
@@ -78,6 +79,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                        _i, _i, _i, _i, _i, _i, _i, _i, _f,
                                        _vp, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.dspark_propose_d2t.restype = _i
+    lib.dspark_propose_adaptive.argtypes = [_vp, _i, _vp, _vp, _vp, _vp, _vp, _vp,
+                                            _i, _i, _i, _i, _i, _i, _i, _vp, _vp,
+                                            _vp, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp]
+    lib.dspark_propose_adaptive.restype = _i
     lib.dspark_verify.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp]
     lib.dspark_verify.restype = _i
     lib.dspark_read_flags.argtypes = [_vp, ctypes.POINTER(ctypes.c_uint32), _vp]
@@ -193,6 +198,38 @@ def propose(hidden, lm_head, markov_w1, markov_w2, anchors, *, layout="anchor_fi
         _ptr(out.lengths), _stream(hidden, stream))
     if st != OK:
         raise DsparkError(st, "dspark_propose")
+    return out
+
+
+def propose_adaptive(hidden, lm_head, markov_w1, markov_w2, anchors, conf_w, p_min, *,
+                     layout="anchor_first", top_k=1, block_top_k=None, lm_head_bias=None,
+                     out: Optional[Outputs] = None, stream=None) -> Outputs:
+    """Run dspark_propose_adaptive: ``p_min`` is a device fp32 [B] tensor of
+    per-block thresholds, ``block_top_k`` an optional device int32 [B]."""
+    torch = _torch()
+    lib = load_library()
+    B, L, H = hidden.shape
+    V = lm_head.shape[0]
+    r = 0 if markov_w1 is None else markov_w1.shape[1]
+    _check_dev("hidden", hidden, hidden.dtype)
+    _check_dev("lm_head", lm_head, torch.bfloat16, (V, H))
+    _check_dev("lm_head_bias", lm_head_bias, torch.float32, (V,))
+    _check_dev("markov_w1", markov_w1, torch.bfloat16, (V, r))
+    _check_dev("markov_w2", markov_w2, torch.bfloat16, (V, r))
+    _check_dev("conf_w", conf_w, torch.bfloat16, (H,))
+    _check_dev("anchors", anchors, torch.int32, (B,))
+    _check_dev("p_min", p_min, torch.float32, (B,))
+    _check_dev("block_top_k", block_top_k, torch.int32, (B,))
+    if out is None:
+        out = Outputs(B, L, V, top_k, layout, hidden.device)
+    st = lib.dspark_propose_adaptive(
+        _ptr(hidden), _hidden_dtype(hidden), _ptr(lm_head), _ptr(lm_head_bias), _ptr(markov_w1),
+        _ptr(markov_w2), _ptr(conf_w), _ptr(anchors), B, L, H, V, r, LAYOUTS[layout], top_k,
+        _ptr(p_min), _ptr(block_top_k), _ptr(out.logits), _ptr(out.workspace),
+        out.workspace.numel(), _ptr(out.tokens), _ptr(out.candidates), _ptr(out.cand_logits),
+        _ptr(out.conf), _ptr(out.lengths), _stream(hidden, stream))
+    if st != OK:
+        raise DsparkError(st, "dspark_propose_adaptive")
     return out
 
 

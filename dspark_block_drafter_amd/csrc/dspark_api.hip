@@ -72,10 +72,17 @@ int check_chain_args(int V, int r, int top_k, float p_min, const void* w1, const
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP; }
 
-// The chain over V columns; with d2t (a reduced draft vocabulary) column c is
-// target id d2t[c] and previous tokens index markov_w1 in [0, vocab).
+// Options of the chain beyond the plain step.
+struct ChainExtras {
+    const int64_t* d2t = nullptr;     // reduced draft vocabulary: column c is target id d2t[c]
+    int vocab = 0;                    // target vocabulary (rows of markov_w1); 0: V
+    const float* p_min_b = nullptr;   // adaptive gate: per-block thresholds, conf before the chain
+    const int32_t* top_k_b = nullptr; // adaptive: candidates kept per block
+};
+
+// The chain over V columns.
 int run_chain(const float* logits, const void* hidden, int hidden_dtype, const uint16_t* w1,
-              const uint16_t* w2, const int64_t* d2t, int vocab, const uint16_t* conf_w,
+              const uint16_t* w2, const ChainExtras& x, const uint16_t* conf_w,
               const int32_t* anchors, int B, int L, int H, int V, int r, int layout, int top_k,
               float p_min, void* workspace, int32_t* tokens, int32_t* candidates,
               float* cand_logits, float* conf, int32_t* lengths, hipStream_t stream) {
@@ -88,8 +95,10 @@ int run_chain(const float* logits, const void* hidden, int hidden_dtype, const u
     c.logits = logits;
     c.w1 = w1;
     c.w2 = w2;
-    c.d2t = d2t;
-    c.vocab = vocab;
+    c.d2t = x.d2t;
+    c.vocab = x.vocab > 0 ? x.vocab : V;
+    // the word after the flags word holds the gate's slot count
+    c.stop = x.p_min_b ? reinterpret_cast<const int32_t*>(ws + sizeof(uint32_t)) : nullptr;
     c.anchors = anchors;
     c.winners = reinterpret_cast<unsigned long long*>(ws + wl.winners_off);
     c.partials = top_k > 1 ? reinterpret_cast<unsigned long long*>(ws + wl.partials_off) : nullptr;
@@ -103,14 +112,32 @@ int run_chain(const float* logits, const void* hidden, int hidden_dtype, const u
     c.nwg = chain_workgroups(B, V, r);
 
     hipError_t e = launch_chain_init(c, stream);
+    if (e == hipSuccess && x.p_min_b) {
+        GateArgs g;
+        g.hidden = hidden;
+        g.conf_w = conf_w;
+        g.p_min = x.p_min_b;
+        g.conf = conf;
+        g.lengths = lengths;
+        g.stop = reinterpret_cast<int32_t*>(ws + sizeof(uint32_t));
+        g.B = B;
+        g.L = L;
+        g.H = H;
+        g.n_pred = n_pred;
+        g.i_first = i_first;
+        g.hidden_f32 = hidden_dtype == DSPARK_HIDDEN_F32;
+        e = launch_gate(g, stream);
+    }
     for (int j = 0; j < n_pred && e == hipSuccess; ++j) e = launch_chain_step(c, j, stream);
     if (e != hipSuccess) return DSPARK_ERR_HIP;
 
     FinalArgs f;
     f.winners = c.winners;
     f.partials = c.partials;
-    f.d2t = d2t;
+    f.d2t = x.d2t;
     f.V = V;
+    f.gated = x.p_min_b != nullptr;
+    f.top_k_b = x.top_k_b;
     f.hidden = hidden;
     f.conf_w = conf_w;
     f.tokens = tokens;
@@ -183,7 +210,7 @@ int dspark_chain(const float* logits, const void* hidden, int hidden_dtype,
     if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return DSPARK_ERR_WORKSPACE;
     if (workspace_bytes < dspark_workspace_bytes(B, L, V, top_k, layout)) return DSPARK_ERR_WORKSPACE;
     if (!aligned16(logits)) return DSPARK_ERR_UNSUPPORTED;
-    return run_chain(logits, hidden, hidden_dtype, markov_w1, markov_w2, nullptr, V, conf_w,
+    return run_chain(logits, hidden, hidden_dtype, markov_w1, markov_w2, ChainExtras(), conf_w,
                      anchors, B, L, H, V, r, layout, top_k, p_min, workspace, tokens, candidates,
                      cand_logits, conf, lengths, static_cast<hipStream_t>(stream));
 }
@@ -211,7 +238,7 @@ int dspark_propose(const void* hidden, int hidden_dtype, const uint16_t* lm_head
     st = dspark_logits(hidden, hidden_dtype, lm_head, lm_head_bias, B, L, H, V, layout, logits,
                        stream);
     if (st != DSPARK_OK) return st;
-    return run_chain(logits, hidden, hidden_dtype, markov_w1, markov_w2, nullptr, V, conf_w,
+    return run_chain(logits, hidden, hidden_dtype, markov_w1, markov_w2, ChainExtras(), conf_w,
                      anchors, B, L, H, V, r, layout, top_k, p_min, workspace, tokens, candidates,
                      cand_logits, conf, lengths, static_cast<hipStream_t>(stream));
 }
@@ -241,9 +268,44 @@ int dspark_propose_d2t(const void* hidden, int hidden_dtype, const uint16_t* lm_
 
     st = dspark_logits(hidden, hidden_dtype, lm_head, nullptr, B, L, H, D, layout, logits, stream);
     if (st != DSPARK_OK) return st;
-    return run_chain(logits, hidden, hidden_dtype, markov_w1, markov_w2, d2t, V, conf_w, anchors,
-                     B, L, H, D, r, layout, top_k, p_min, workspace, tokens, candidates,
-                     cand_logits, conf, lengths, static_cast<hipStream_t>(stream));
+    ChainExtras x;
+    x.d2t = d2t;
+    x.vocab = V;
+    return run_chain(logits, hidden, hidden_dtype, markov_w1, markov_w2, x, conf_w, anchors, B, L,
+                     H, D, r, layout, top_k, p_min, workspace, tokens, candidates, cand_logits,
+                     conf, lengths, static_cast<hipStream_t>(stream));
+}
+
+int dspark_propose_adaptive(const void* hidden, int hidden_dtype, const uint16_t* lm_head,
+                            const float* lm_head_bias, const uint16_t* markov_w1,
+                            const uint16_t* markov_w2, const uint16_t* conf_w,
+                            const int32_t* anchors, int B, int L, int H, int V, int r, int layout,
+                            int top_k, const float* p_min, const int32_t* block_top_k,
+                            float* logits, void* workspace, size_t workspace_bytes,
+                            int32_t* tokens, int32_t* candidates, float* cand_logits, float* conf,
+                            int32_t* lengths, void* stream) {
+    int st = check_sizes(B, L, H, V, layout, hidden_dtype);
+    if (st != DSPARK_OK) return st;
+    st = check_chain_args(V, r, top_k, 0.0f, markov_w1, markov_w2);
+    if (st != DSPARK_OK) return st;
+    if (!hidden || !lm_head || !conf_w || !p_min || !logits || !anchors || !tokens ||
+        !candidates || !lengths)
+        return DSPARK_ERR_INVALID_ARG;
+    if (!aligned16(hidden) || !aligned16(lm_head) || !aligned16(logits) || !aligned16(conf_w))
+        return DSPARK_ERR_UNSUPPORTED;
+    if (!workspace) return DSPARK_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return DSPARK_ERR_WORKSPACE;
+    if (workspace_bytes < dspark_workspace_bytes(B, L, V, top_k, layout)) return DSPARK_ERR_WORKSPACE;
+
+    st = dspark_logits(hidden, hidden_dtype, lm_head, lm_head_bias, B, L, H, V, layout, logits,
+                       stream);
+    if (st != DSPARK_OK) return st;
+    ChainExtras x;
+    x.p_min_b = p_min;
+    x.top_k_b = block_top_k;
+    return run_chain(logits, hidden, hidden_dtype, markov_w1, markov_w2, x, conf_w, anchors, B, L,
+                     H, V, r, layout, top_k, 0.0f, workspace, tokens, candidates, cand_logits,
+                     conf, lengths, static_cast<hipStream_t>(stream));
 }
 
 int dspark_verify(const int32_t* candidates, const int32_t* lengths, const int32_t* target, int B,

@@ -64,6 +64,7 @@ struct ChainArgs {
     int32_t* lengths;          // [B], set to n_pred here, cut by the confidence head later
     int B, V, r, n_pred, top_k, nwg;
     int vocab;                 // target vocabulary size (== V without d2t)
+    const int32_t* stop;       // adaptive gate: slots from *stop on are skipped (nullptr: none)
 };
 hipError_t launch_chain_init(const ChainArgs& a, hipStream_t stream);
 hipError_t launch_chain_step(const ChainArgs& a, int j, hipStream_t stream);
@@ -84,8 +85,22 @@ struct FinalArgs {
     int V;                     // chain columns (keys outside [0, V) are never mapped)
     int hidden_f32;
     float p_min;
+    int gated;                 // conf and lengths came from the adaptive gate; mask cut slots
+    const int32_t* top_k_b;    // [B] candidates kept per block, or nullptr (all top_k)
 };
 hipError_t launch_finalize(const FinalArgs& a, hipStream_t stream);
+
+// ---- adaptive gate -------------------------------------------------------------
+struct GateArgs {
+    const void* hidden;
+    const uint16_t* conf_w;    // [H]
+    const float* p_min;        // [B] per-block thresholds
+    float* conf;               // [B, n_pred] or nullptr
+    int32_t* lengths;          // [B], preset to n_pred
+    int32_t* stop;             // one word: max over blocks of lengths
+    int B, L, H, n_pred, i_first, hidden_f32;
+};
+hipError_t launch_gate(const GateArgs& g, hipStream_t stream);
 
 // ---- greedy verification ---------------------------------------------------------
 struct VerifyArgs {

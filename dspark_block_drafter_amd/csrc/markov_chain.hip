@@ -182,6 +182,8 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lrow = lane & 31, lhalf = lane >> 5;
     const int vb = wave % VW, nbw = wave / VW;       // this wave's 32-column block / block group
+    // adaptive gate: every block was cut before this slot
+    if (a.stop && j >= *a.stop) return;
     const int bbase = blockIdx.y * NB * 32;
     const int B = a.B, V = a.V, r = a.r;
     const int nT = (V + TS - 1) / TS, G = gridDim.x, g = blockIdx.x;
@@ -441,6 +443,7 @@ template <int NB, int KL, int RS>
 __global__ __launch_bounds__(256) void chain_step_direct(ChainArgs a, int j) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lrow = lane & 31, lhalf = lane >> 5;
+    if (a.stop && j >= *a.stop) return;   // adaptive gate: every block was cut
     const int bbase = blockIdx.y * NB * 32;
     const int B = a.B, V = a.V, r = a.r;
     __shared__ u64 s_list[kWaves][NB * 32][KL];
@@ -502,6 +505,40 @@ __global__ __launch_bounds__(256) void chain_step_direct(ChainArgs a, int j) {
 
 // ---- final assembly: one workgroup per (slot, block) --------------------------
 
+// Confidence of one slot on one wave: float(sigmoid(hidden_row . conf_w)),
+// fp32 hidden rounded to bf16 first.
+__device__ __forceinline__ float slot_conf(const void* hidden, int hidden_f32, const uint16_t* conf_w,
+                                           long row, int H, int lane) {
+    float s = 0.0f;
+    for (int h = lane * 8; h < H; h += 64 * 8) {
+        const u32x4 cw = *reinterpret_cast<const u32x4*>(conf_w + h);
+        float x[8];
+        if (hidden_f32) {
+            const f32x4* hp = reinterpret_cast<const f32x4*>(static_cast<const float*>(hidden) + row * H + h);
+            const f32x4 x0 = hp[0], x1 = hp[1];
+            const uint32_t p0 = pack_bf16x2(x0[0], x0[1]), p1 = pack_bf16x2(x0[2], x0[3]);
+            const uint32_t p2 = pack_bf16x2(x1[0], x1[1]), p3 = pack_bf16x2(x1[2], x1[3]);
+            x[0] = bf16_lo(p0); x[1] = bf16_hi(p0); x[2] = bf16_lo(p1); x[3] = bf16_hi(p1);
+            x[4] = bf16_lo(p2); x[5] = bf16_hi(p2); x[6] = bf16_lo(p3); x[7] = bf16_hi(p3);
+        } else {
+            const u32x4 hv = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(hidden) + row * H + h);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                x[2 * q] = bf16_lo(hv[q]);
+                x[2 * q + 1] = bf16_hi(hv[q]);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            s += x[2 * q] * bf16_lo(cw[q]);
+            s += x[2 * q + 1] * bf16_hi(cw[q]);
+        }
+    }
+#pragma unroll
+    for (int mask = 32; mask >= 1; mask >>= 1) s += __shfl_xor(s, mask, 64);
+    return 1.0f / (1.0f + expf(-s));
+}
+
 // Output id of a key: the target id of its column (the column without d2t).
 __device__ __forceinline__ int final_token(const FinalArgs& a, u64 key) {
     const int c = key_id(key);
@@ -521,6 +558,18 @@ __global__ __launch_bounds__(256) void finalize(FinalArgs a) {
     const long o = (long)b * n + j;
     const u64 win = a.winners[(long)j * B + b];
     __shared__ u64 s_list[kWaves][KL];
+
+    // Adaptive gate: a slot past its block's cut was not drafted, and a block
+    // keeps only its own number of candidates.
+    const int kb = a.top_k_b ? min(max(a.top_k_b[b], 1), k) : k;
+    if (a.gated && j >= a.lengths[b]) {
+        for (int i = threadIdx.x; i < k; i += 256) {
+            a.candidates[o * k + i] = -1;
+            if (a.cand_logits) a.cand_logits[o * k + i] = -INFINITY;
+        }
+        if (threadIdx.x == 0) a.tokens[o] = -1;
+        return;
+    }
 
     if (k == 1) {
         if (threadIdx.x == 0) {
@@ -562,51 +611,52 @@ __global__ __launch_bounds__(256) void finalize(FinalArgs a) {
 #pragma unroll
             for (int i = 0; i < KL; ++i) {
                 if (i < k) {
-                    a.candidates[o * k + i] = final_token(a, list[i]);
-                    if (a.cand_logits) a.cand_logits[o * k + i] = key_score(list[i]);
+                    a.candidates[o * k + i] = i < kb ? final_token(a, list[i]) : -1;
+                    if (a.cand_logits) a.cand_logits[o * k + i] = i < kb ? key_score(list[i]) : -INFINITY;
                 }
             }
         }
     }
 
-    // Confidence head on wave 1 (wave 0 may still be writing candidates).
-    if (wave == 1 % kWaves) {
+    // Confidence head on wave 1 (wave 0 may still be writing candidates);
+    // with the adaptive gate it was computed before the chain.
+    if (!a.gated && wave == 1 % kWaves) {
         float c = 1.0f;
         if (a.conf_w) {
-            const long row = (long)b * a.L + a.i_first + j;
-            float s = 0.0f;
-            for (int h = lane * 8; h < a.H; h += 64 * 8) {
-                const u32x4 cw = *reinterpret_cast<const u32x4*>(a.conf_w + h);
-                float x[8];
-                if (a.hidden_f32) {
-                    const f32x4* hp = reinterpret_cast<const f32x4*>(
-                        static_cast<const float*>(a.hidden) + row * a.H + h);
-                    const f32x4 x0 = hp[0], x1 = hp[1];
-                    const uint32_t p0 = pack_bf16x2(x0[0], x0[1]), p1 = pack_bf16x2(x0[2], x0[3]);
-                    const uint32_t p2 = pack_bf16x2(x1[0], x1[1]), p3 = pack_bf16x2(x1[2], x1[3]);
-                    x[0] = bf16_lo(p0); x[1] = bf16_hi(p0); x[2] = bf16_lo(p1); x[3] = bf16_hi(p1);
-                    x[4] = bf16_lo(p2); x[5] = bf16_hi(p2); x[6] = bf16_lo(p3); x[7] = bf16_hi(p3);
-                } else {
-                    const u32x4 hv = *reinterpret_cast<const u32x4*>(
-                        static_cast<const uint16_t*>(a.hidden) + row * a.H + h);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        x[2 * q] = bf16_lo(hv[q]);
-                        x[2 * q + 1] = bf16_hi(hv[q]);
-                    }
-                }
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    s += x[2 * q] * bf16_lo(cw[q]);
-                    s += x[2 * q + 1] * bf16_hi(cw[q]);
-                }
-            }
-#pragma unroll
-            for (int mask = 32; mask >= 1; mask >>= 1) s += __shfl_xor(s, mask, 64);
-            c = 1.0f / (1.0f + expf(-s));
+            c = slot_conf(a.hidden, a.hidden_f32, a.conf_w, (long)b * a.L + a.i_first + j, a.H, lane);
             if (lane == 0 && c < a.p_min) atomicMin(a.lengths + b, j);
         }
         if (lane == 0 && a.conf) a.conf[o] = c;
+    }
+}
+
+// ---- adaptive gate: confidences before the chain ------------------------------
+
+// Slot j of block b on one wave: conf, and lengths[b] lowered to j when
+// conf < p_min[b] (per-block thresholds).
+__global__ __launch_bounds__(64) void conf_gate(GateArgs g) {
+    const int j = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+    const float c = slot_conf(g.hidden, g.hidden_f32, g.conf_w, (long)b * g.L + g.i_first + j, g.H, lane);
+    if (lane == 0) {
+        if (g.conf) g.conf[(long)b * g.n_pred + j] = c;
+        if (c < g.p_min[b]) atomicMin(g.lengths + b, j);
+    }
+}
+
+// The number of slots the chain has to run: the longest surviving block.
+__global__ __launch_bounds__(256) void gate_stop(const int32_t* lengths, int B, int32_t* stop) {
+    __shared__ int s_max[kWaves];
+    int m = 0;
+    for (int b = threadIdx.x; b < B; b += 256) m = max(m, lengths[b]);
+#pragma unroll
+    for (int mask = 32; mask >= 1; mask >>= 1) m = max(m, __shfl_xor(m, mask, kWave));
+    if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int t = s_max[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) t = max(t, s_max[w]);
+        *stop = t;
     }
 }
 
@@ -676,6 +726,12 @@ hipError_t launch_chain_step(const ChainArgs& a, int j, hipStream_t stream) {
     dim3 grid(a.nwg, (a.B + 32 * nb - 1) / (32 * nb));
     const bool pipe = chain_pipelined(a.V);
     return nb == 2 ? step_kl<2>(a, j, grid, pipe, stream) : step_kl<1>(a, j, grid, pipe, stream);
+}
+
+hipError_t launch_gate(const GateArgs& g, hipStream_t stream) {
+    hipLaunchKernelGGL(conf_gate, dim3(g.n_pred, g.B), dim3(64), 0, stream, g);
+    hipLaunchKernelGGL(gate_stop, dim3(1), dim3(256), 0, stream, g.lengths, g.B, g.stop);
+    return hipGetLastError();
 }
 
 hipError_t launch_finalize(const FinalArgs& a, hipStream_t stream) {

@@ -211,6 +211,40 @@ int dspark_propose_d2t(const void* hidden, int hidden_dtype, const uint16_t* lm_
                        void* stream);
 
 /*
+ * The proposal step with the confidence gate in front of the chain and
+ * per-block settings (per-request heterogeneity). The confidence of every
+ * slot is computed first and each block is cut at its first slot below its
+ * own threshold p_min[b]; the chain then runs only as many slots as the
+ * longest surviving block, and slots past a block's cut are reported as not
+ * drafted. This wires the adaptive block length that lucebox PR #626
+ * "feat(qwen38): add adaptive concurrent DSpark speculation" leaves unwired
+ * (description: the confidence-gate adaptive block length, the per-request
+ * override of the decode mode), with the threshold semantics of llama.cpp
+ * commit 6fed9f6 "spec: add DSpark speculative decoding", items "spec: add
+ * confidence-based draft pruning for DSpark" and "dspark: fold conf_min into
+ * p_min".
+ *
+ *   conf_w        DEVICE bf16 [H]; required (the gate needs it).
+ *   p_min         DEVICE fp32 [B]: the threshold of each block (not NaN).
+ *   block_top_k   DEVICE int32 [B] or NULL: candidates kept per block,
+ *                 clamped to [1, top_k]; top_k sizes the candidate arrays.
+ *   tokens        slots j >= lengths[b] hold -1.
+ *   candidates    slots j >= lengths[b], and ranks >= block_top_k[b], hold -1;
+ *   cand_logits   -INFINITY there.
+ * Every other argument is as in dspark_propose; on the slots a block keeps,
+ * the outputs equal dspark_propose's with that block's p_min and top_k.
+ * Returns a dspark_status.
+ */
+int dspark_propose_adaptive(const void* hidden, int hidden_dtype, const uint16_t* lm_head,
+                            const float* lm_head_bias, const uint16_t* markov_w1,
+                            const uint16_t* markov_w2, const uint16_t* conf_w,
+                            const int32_t* anchors, int B, int L, int H, int V, int r, int layout,
+                            int top_k, const float* p_min, const int32_t* block_top_k,
+                            float* logits, void* workspace, size_t workspace_bytes,
+                            int32_t* tokens, int32_t* candidates, float* cand_logits, float* conf,
+                            int32_t* lengths, void* stream);
+
+/*
  * Greedy verification of a proposal against the target's tokens: the target
  * keeps the longest drafted prefix it would have produced itself, so greedy
  * speculation stays lossless (llama.cpp commit 6fed9f6 "spec: add DSpark

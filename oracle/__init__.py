@@ -83,6 +83,10 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
                                              _i, _i, _i, _i, _i, _i, _i, ctypes.c_float, _i,
                                              _f64p, _i32p, _i32p, _f32p, _f32p, _i32p]
     lib.oracle_propose_block_d2t.restype = _i
+    lib.oracle_propose_block_gated.argtypes = [_vp, _i, _u16p, _f32p, _u16p, _u16p, _u16p, _i32p,
+                                               _i, _i, _i, _i, _i, _i, _i, ctypes.c_float, _i,
+                                               _f64p, _i32p, _i32p, _f32p, _f32p, _i32p]
+    lib.oracle_propose_block_gated.restype = _i
     lib.oracle_verify.argtypes = [_i32p, _i32p, _i32p, _i, _i, _i, _i, _i32p, _i64p]
     lib.oracle_verify.restype = _i
     return lib
@@ -214,6 +218,30 @@ class Oracle:
             _p(length, _i32p))
         if st != 0:
             raise ValueError("oracle_propose_block rejected its arguments")
+        return {"logits": z, "tokens": tokens, "candidates": cand, "cand_logits": cval,
+                "conf": conf, "length": int(length[0])}
+
+    def propose_block_gated(self, inp, b: int, p_min: float, kb: int,
+                            keep_logits: bool = True) -> dict:
+        """Block b under the adaptive gate with its own threshold and kb candidates."""
+        c = inp.cfg
+        n, k = c.n_pred, c.top_k
+        z = np.empty((n, c.V), dtype=np.float64) if keep_logits else None
+        tokens = np.empty(n, dtype=np.int32)
+        cand = np.empty((n, k), dtype=np.int32)
+        cval = np.empty((n, k), dtype=np.float32)
+        conf = np.empty(n, dtype=np.float32)
+        length = np.zeros(1, dtype=np.int32)
+        st = self.lib.oracle_propose_block_gated(
+            inp.hidden.ctypes.data, int(inp.hidden_f32), _p(inp.lm_head, _u16p),
+            _p(inp.lm_head_bias, _f32p), _p(inp.markov_w1, _u16p), _p(inp.markov_w2, _u16p),
+            _p(inp.conf_w, _u16p), _p(inp.anchors, _i32p), c.L, c.H, c.V, c.r,
+            c.i_first_pred, k, int(kb), ctypes.c_float(p_min), b,
+            _p(z, _f64p) if z is not None else ctypes.cast(None, _f64p),
+            _p(tokens, _i32p), _p(cand, _i32p), _p(cval, _f32p), _p(conf, _f32p),
+            _p(length, _i32p))
+        if st != 0:
+            raise ValueError("oracle_propose_block_gated rejected its arguments")
         return {"logits": z, "tokens": tokens, "candidates": cand, "cand_logits": cval,
                 "conf": conf, "length": int(length[0])}
 

@@ -39,6 +39,12 @@
  * chosen draft ids are reported as target ids. Every target id off the table
  * has no score, so it can never be chosen.
  *
+ * Adaptive block length: the confidence of every slot is known before the
+ * chain runs, so a block cut at slot `length` only drafts its first `length`
+ * slots; each block may carry its own threshold and its own number of
+ * candidates (lucebox PR #626 description: the confidence-gate adaptive block
+ * length and the per-request override).
+ *
  * Verification: greedy speculation is lossless because the target keeps only
  * the longest drafted prefix it would have produced itself (llama.cpp commit
  * 6fed9f6, the in-graph chain item: verification unchanged from DFlash); with
@@ -410,4 +416,55 @@ int oracle_verify(const int32_t* cand, const int32_t* lengths, const int32_t* ta
         totals[1] += len;
     }
     return ORACLE_OK;
+}
+
+/* Block b under the adaptive gate: its confidences and cut first (threshold
+ * p_min of this block), then the chain over the surviving slots only, with kb
+ * candidates per slot. Slots past the cut hold token -1 and candidates -1
+ * (value -INFINITY), ranks kb .. top_k-1 likewise; z (may be NULL) receives
+ * the projections [n_pred][V] of every slot. */
+int oracle_propose_block_gated(const void* hidden, int hidden_is_f32, const uint16_t* lm_head,
+                               const float* bias, const uint16_t* w1, const uint16_t* w2,
+                               const uint16_t* conf_w, const int32_t* anchors, int L, int H, int V,
+                               int r, int i_first_pred, int top_k, int kb, float p_min, int b,
+                               double* z, int32_t* tokens, int32_t* cand, float* cand_val,
+                               float* conf, int32_t* length)
+{
+    const int n_pred = L - i_first_pred;
+    if (!conf_w || kb < 1 || kb > top_k || top_k > V || n_pred < 1)
+        return ORACLE_ERR;
+    for (int j = 0; j < n_pred; ++j)
+        conf[j] = oracle_conf(hidden, hidden_is_f32, conf_w, L, H, i_first_pred, b, j);
+    const int len = oracle_truncate(conf, n_pred, p_min);
+    *length = len;
+    for (int j = 0; j < n_pred; ++j) {
+        tokens[j] = -1;
+        for (int t = 0; t < top_k; ++t) {
+            cand[(size_t)j * top_k + t] = -1;
+            cand_val[(size_t)j * top_k + t] = -INFINITY;
+        }
+    }
+    double* zz = z ? z : (double*)malloc(sizeof(double) * (size_t)n_pred * (size_t)V);
+    if (!zz)
+        return ORACLE_ERR;
+    int st = oracle_block_logits(hidden, hidden_is_f32, lm_head, bias, L, H, V, i_first_pred, b, zz);
+    if (st == ORACLE_OK && len > 0) {
+        int32_t* c = (int32_t*)malloc(sizeof(int32_t) * (size_t)len * kb);
+        float* cv = (float*)malloc(sizeof(float) * (size_t)len * kb);
+        if (!c || !cv)
+            st = ORACLE_ERR;
+        else
+            st = oracle_block_chain(zz, w1, w2, V, r, anchors[b], len, kb, tokens, c, cv);
+        if (st == ORACLE_OK)
+            for (int j = 0; j < len; ++j)
+                for (int t = 0; t < kb; ++t) {
+                    cand[(size_t)j * top_k + t] = c[(size_t)j * kb + t];
+                    cand_val[(size_t)j * top_k + t] = cv[(size_t)j * kb + t];
+                }
+        free(c);
+        free(cv);
+    }
+    if (!z)
+        free(zz);
+    return st;
 }

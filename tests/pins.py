@@ -503,4 +503,37 @@ def pin_verify_bruteforce(orc):
         assert acc.tolist() == [min(max(int(l), 0), n) for l in lengths]
 
 
+def pin_gated_equals_masked_full_step(orc):
+    """Under the adaptive gate a block drafts only the slots that survive its
+    own threshold, with its own number of candidates: on those slots the
+    outputs are the plain step's (same prefix of the chain, top-k a prefix of
+    the larger top-k), everything past the cut is -1 / -inf, and the cut is
+    the plain step's cut under that threshold."""
+    from synthetic.inputs import BONUS_ANCHOR
+    cases = [make_small(4, 6, 64, 900, 16, top_k=4, conf=True, conf_trend=True, seed=51),
+             make_small(3, 7, 48, 500, 8, top_k=3, conf=True, conf_trend=True,
+                        layout=BONUS_ANCHOR, seed=52)]
+    for inp in cases:
+        c = inp.cfg
+        for b in range(c.B):
+            for p_min, kb in ((0.0, c.top_k), (0.5, 2), (0.7, 1), (0.99, c.top_k)):
+                full = orc.propose_block(replace(inp, cfg=replace(c, p_min=p_min)), b)
+                g = orc.propose_block_gated(inp, b, p_min, kb)
+                n = g["length"]
+                assert n == full["length"]
+                assert np.array_equal(g["conf"], full["conf"])
+                assert np.array_equal(g["logits"], full["logits"])
+                assert np.array_equal(g["tokens"][:n], full["tokens"][:n])
+                assert np.all(g["tokens"][n:] == -1)
+                assert np.array_equal(g["candidates"][:n, :kb], full["candidates"][:n, :kb])
+                assert np.array_equal(g["cand_logits"][:n, :kb], full["cand_logits"][:n, :kb])
+                assert np.all(g["candidates"][:, kb:] == -1) and np.all(g["candidates"][n:] == -1)
+                assert np.all(np.isneginf(g["cand_logits"][:, kb:]))
+                assert np.all(np.isneginf(g["cand_logits"][n:]))
+    # the thresholds used above do cut some blocks early and keep others whole
+    inp = cases[0]
+    lens = [orc.propose_block_gated(inp, b, 0.5, 1, keep_logits=False)["length"] for b in range(4)]
+    assert min(lens) < inp.cfg.n_pred
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

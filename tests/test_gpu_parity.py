@@ -223,6 +223,76 @@ def test_d2t_full_size_gemma(dev, orc):
     check(orc, inp, g, blocks=[0, 3])
 
 
+# ---- adaptive gate: per-block thresholds and candidate counts -------------------
+
+ADAPTIVE = {
+    # trend 0.9 -> 0.3 over the slots; thresholds spread over the blocks
+    "adaptive_k4": lambda: make_small(6, 8, 96, 3000, 16, top_k=4, conf=True, conf_trend=True,
+                                      seed=61),
+    "adaptive_bonus_direct": lambda: make_small(5, 7, 64, 1001, 8, top_k=3, conf=True,
+                                                conf_trend=True, layout=BONUS_ANCHOR, seed=62),
+    "adaptive_B70": lambda: make_small(70, 5, 64, 2048, 16, top_k=2, conf=True, conf_trend=True,
+                                       seed=63),
+}
+
+
+def _run_adaptive(inp, p_min_b, top_k_b):
+    import torch
+
+    import dspark_block_drafter_amd as dsp
+    from devutil import to_device, to_host
+    d = to_device(inp)
+    c = inp.cfg
+    res = dsp.propose_adaptive(d["hidden"], d["lm_head"], d["markov_w1"], d["markov_w2"],
+                               d["anchors"], d["conf_w"], torch.from_numpy(p_min_b).to("cuda:0"),
+                               layout=c.layout, top_k=c.top_k, lm_head_bias=d["lm_head_bias"],
+                               block_top_k=None if top_k_b is None else
+                               torch.from_numpy(top_k_b).to("cuda:0"))
+    torch.cuda.synchronize()
+    assert dsp.read_flags(res) == 0
+    return to_host(res)
+
+
+@pytest.mark.parametrize("name", sorted(ADAPTIVE))
+@pytest.mark.parametrize("thresholds", ["spread", "cut_mid", "all_cut_early", "none_cut"])
+def test_adaptive_against_full_step_and_oracle(dev, orc, name, thresholds):
+    """On every slot a block keeps, the gated step equals the plain step bit
+    for bit (tokens, candidates up to the block's count, values, conf); past
+    the cut it reports -1 / -inf; the cuts equal the oracle's under each
+    block's threshold (a confidence within 1e-3 of its threshold may go
+    either way). The plain step itself is checked against the oracle."""
+    inp = ADAPTIVE[name]()
+    c = inp.cfg
+    rng = np.random.default_rng(len(name))
+    p_min_b = {"spread": rng.uniform(0.2, 0.95, c.B),
+               "cut_mid": np.full(c.B, 0.6),
+               "all_cut_early": np.full(c.B, 0.97),
+               "none_cut": np.zeros(c.B)}[thresholds].astype(np.float32)
+    top_k_b = rng.integers(1, c.top_k + 1, c.B).astype(np.int32)
+    _say(f"[adaptive] {name} {thresholds}: {c}")
+    g = _run_adaptive(inp, p_min_b, top_k_b)
+    full = _gpu(inp)            # p_min 0: every slot drafted
+    check(orc, inp, full)
+    assert np.array_equal(g["conf"], full["conf"])
+    assert np.array_equal(g["logits"], full["logits"])
+    for b in range(c.B):
+        n, kb = int(g["lengths"][b]), int(top_k_b[b])
+        o = orc.propose_block_gated(inp, b, float(p_min_b[b]), kb, keep_logits=False)
+        if n != o["length"]:
+            lo = min(n, o["length"])
+            assert abs(float(o["conf"][lo]) - float(p_min_b[b])) < 1e-3, (b, n, o["length"])
+        assert np.array_equal(g["tokens"][b, :n], full["tokens"][b, :n])
+        assert np.all(g["tokens"][b, n:] == -1)
+        assert np.array_equal(g["candidates"][b, :n, :kb], full["candidates"][b, :n, :kb])
+        assert np.array_equal(g["cand_logits"][b, :n, :kb], full["cand_logits"][b, :n, :kb])
+        assert np.all(g["candidates"][b, n:] == -1) and np.all(g["candidates"][b, :, kb:] == -1)
+        assert np.all(np.isneginf(g["cand_logits"][b, n:]))
+    if thresholds in ("cut_mid", "all_cut_early"):
+        assert g["lengths"].max() < c.n_pred     # the chain stopped early
+    if thresholds == "none_cut":
+        assert np.all(g["lengths"] == c.n_pred)
+
+
 # ---- greedy verification of the lattice -----------------------------------------
 
 def _verify_tables(B, n, k, vocab, seed, p_hit=0.8):

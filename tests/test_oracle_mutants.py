@@ -50,6 +50,11 @@ MUTANTS = {
     "verify_counts_all_matches": ("            if (!found)\n                break;\n            ++m;",
                                   "            if (!found) {\n                ++m;\n                continue;\n            }\n            ++m;"),
     "verify_total_unclamped": ("        totals[1] += len;", "        totals[1] += lengths[b];"),
+    "gated_chain_ignores_cut": ("st = oracle_block_chain(zz, w1, w2, V, r, anchors[b], len, kb, tokens, c, cv);",
+                                "st = oracle_block_chain(zz, w1, w2, V, r, anchors[b], len, kb, tokens, c, cv); tokens[len - 1] = 0;"),
+    "gated_keeps_all_candidates": ("                for (int t = 0; t < kb; ++t) {\n                    cand[(size_t)j * top_k + t]",
+                                   "                for (int t = 0; t < kb - 1; ++t) {\n                    cand[(size_t)j * top_k + t]"),
+    "gated_no_fill": ("            cand_val[(size_t)j * top_k + t] = -INFINITY;", "            cand_val[(size_t)j * top_k + t] = 0.0f;"),
     "hidden_f32_truncated": ("x[h] = bf16_value(oracle_bf16_round(p[h]));",
                              "x[h] = bf16_value((uint16_t)(*(const uint32_t*)&p[h] >> 16));"),
 }
