@@ -237,7 +237,9 @@ def main() -> int:
         gemm_roof = {"bound": "hbm", "achieved": gemm_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gemm_gbs / PEAK_HBM_GBS}
     # chain: per slot the B logits rows and markov_w2 are streamed, plus B rank-r gathers
-    chain_bytes = n * (B * V * 4 + V * r * 2 + B * r * 2)
+    # (the adaptive gate runs the chain only up to the longest surviving block)
+    slots_run = int(out.lengths.max().item()) if args.adaptive else n
+    chain_bytes = slots_run * (B * V * 4 + V * r * 2 + B * r * 2)
     chain_gbs = chain_bytes / (chain_ms * 1e-3) / 1e9
 
     res = {
@@ -267,7 +269,9 @@ def main() -> int:
                            "bytes": chain_bytes, "kernels": "chain_init + chain_step x n_pred + finalize",
                            "us": chain_ms * 1e3},
         "wall_ms_per_step": 1e3 * wall / args.steps,
-        "verify": {"kernel": "verify_walk", "us": verify_us, "lattice": True,
+        # call time of dspark_verify through the binding, host enqueue included
+        # (its two kernels take a few microseconds: see the kernel statistics)
+        "verify": {"kernels": "verify_walk + verify_totals", "call_us": verify_us, "lattice": True,
                    "submitted_slots": walked[1]},
     }
     if not args.no_cpu_baseline:
