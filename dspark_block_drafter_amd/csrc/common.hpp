@@ -123,5 +123,6 @@ __device__ __forceinline__ void block_barrier() {
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef __attribute__((address_space(3))) char lds_char;
 
 }  // namespace dspark

@@ -213,6 +213,14 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
             dst[i] = W_SLOTS + (inst - W_INST) * 64;
         }
     }
+    // The copies into the ring address it through a base the compiler cannot
+    // trace to the array: a copy it can attribute to the ring would make the
+    // next LDS read of the ring wait for every load in flight (vmcnt(0)),
+    // which drains the ring. The explicit waits below order the reads. (The
+    // address arithmetic stays inline: moved into a helper called from the
+    // lambdas, the host pass stops emitting this kernel's launch stub.)
+    lds_char* ring_dma = (lds_char*)(lds_ptr)&ring[0][0];
+    asm volatile("" : "+s"(ring_dma));
     // Columns past V: markov_w2 rows are clamped to row V-1, logits to the
     // last 16-byte chunk of the row; such columns are never scored.
     auto issue = [&](int st, int t) __attribute__((always_inline)) {
@@ -221,7 +229,7 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
 #pragma unroll
             for (int i = 0; i < LW; ++i)
                 __builtin_amdgcn_global_load_lds((const void*)(src[i] + (long)t * step[i]),
-                                                 (lds_ptr)&ring[st][dst[i]], 16, 0, 0);
+                                                 (lds_ptr)(ring_dma + (st * STAGE + dst[i]) * 16), 16, 0, 0);
             return;
         }
 #pragma unroll
@@ -235,29 +243,40 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
                 const int c = (slot % LR) ^ swz_rows<LR>(slot / LR);
                 if (v0 + 4 * c > V - 4) p -= (long)(v0 + 4 * c - (V - 4)) * 4;
             }
-            __builtin_amdgcn_global_load_lds((const void*)p, (lds_ptr)&ring[st][dst[i]], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)p, (lds_ptr)(ring_dma + (st * STAGE + dst[i]) * 16), 16, 0, 0);
         }
     };
 
     // Previous token of this lane's block (anchor, or the last slot's argmax).
     const int bme = bbase + nbw * 32 + lrow;
     const int prev = (bme < B && nbw < NB) ? prev_token(a, j, bme, vb == 0) : 0;
-    // First NS - 1 tiles in flight, then the markov_w1 rows of prev (MFMA B
-    // operand). One full wait before the loop: the loop then only ever waits
-    // for ring stages (a register load still in flight there would make every
-    // iteration drain the whole ring).
+    // Tile 0, then the markov_w1 rows of prev (MFMA B operand; their address
+    // needs prev), then tiles 1 .. NS-2. The loop starts once tile 0 and the
+    // W1 rows have landed, with the later tiles still in flight. The W1 rows
+    // travel direct to LDS like the tiles (a register load would need a wait
+    // for every older load, the whole ring), into stage NS-1, which the first
+    // step refills only after the barrier that follows their reads: one copy
+    // per block group, loaded by its first wave. The number of loads issued
+    // after the W1 rows is fixed: a workgroup owns n >= 1 tiles (there are at
+    // most as many workgroups as tiles), and a stage past n - 1 gets a second
+    // copy of the last tile, which no iteration reads. Lanes of blocks past B
+    // read row 0 (their scores are never inserted); chunks past the rank are
+    // zeroed when read.
+    static_assert(NS >= 3, "the first step waits for tile 1 with NS - 3 stages newer");
+    static_assert(NB * RS * 64 <= STAGE, "W1 rows fit stage NS - 1");
+    issue(0, t0);
+    if (RS > 0 && vb == 0 && nbw < NB) {
 #pragma unroll
-    for (int t = 0; t < NS - 1; ++t)
-        if (t < n) issue(t, t0 + t);
-    u32x4 u[RS > 0 ? RS : 1];
-#pragma unroll
-    for (int s = 0; s < RS; ++s) {
-        const int k0 = s * 16 + lhalf * 8;
-        u[s] = (bme < B && nbw < NB && k0 < r)
-                   ? *reinterpret_cast<const u32x4*>(a.w1 + (long)prev * r + k0)
-                   : u32x4{0u, 0u, 0u, 0u};
+        for (int s = 0; s < RS; ++s) {
+            const int k0 = s * 16 + lhalf * 8;
+            __builtin_amdgcn_global_load_lds((const void*)(a.w1 + (long)prev * r + (k0 < r ? k0 : 0)),
+                                             (lds_ptr)(ring_dma + ((NS - 1) * STAGE + (nbw * RS + s) * 64) * 16), 16, 0, 0);
+        }
     }
-    wait_vmcnt<0>();
+#pragma unroll
+    for (int t = 1; t < NS - 1; ++t) issue(t, t0 + min(t, n - 1));
+    wait_vmcnt<(NS - 2) * LW>();
+    u32x4 u[RS > 0 ? RS : 1];   // W1 rows (MFMA B operand), read after the barrier
 
     // MFMA runs on whole waves: only the wave-uniform part of the condition may
     // guard it; blocks past B are masked at the inserts.
@@ -377,32 +396,49 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
             if (lhalf == 0) s_thr[wave][lrow] = own;
         }
     };
-    // one iteration: bring tile it + 1 in and score it, then consume tile it
-    auto step_tile = [&](int it, int& st, const Scores& cur, Scores& nxt) __attribute__((always_inline)) {
+    // one iteration: bring tile it + 1 in and score it, then consume tile it.
+    // The first one refills stage NS - 1 after its barrier, once every wave
+    // holds its W1 rows from there; tiles 1 .. NS - 2 came from the prologue.
+    auto step_tile = [&](int it, int& st, const Scores& cur, Scores& nxt, bool first)
+                         __attribute__((always_inline)) {
         const int nst = st + 1 == NS ? 0 : st + 1;
         if (it + 1 < n) {
-            if (it + NS - 1 < n) issue((st + NS - 1) % NS, t0 + it + NS - 1);
-            wait_stages<LW, NS - 2>(min(NS - 2, n - 2 - it));
+            if (first) {
+                wait_vmcnt<(NS - 3) * LW>();
+            } else {
+                if (it + NS - 1 < n) issue((st + NS - 1) % NS, t0 + it + NS - 1);
+                wait_stages<LW, NS - 2>(min(NS - 2, n - 2 - it));
+            }
             // The logits of tile it were read into registers before this
             // barrier; their reads must have landed before any wave refills
             // that stage after it.
             wait_lds_reads();
             block_barrier();
+            if (first && NS - 1 < n) issue(NS - 1, t0 + NS - 1);
             if (wave_on) score(nst, nxt);
         }
         if (wave_on) consume(it, cur);
         st = nst;
     };
 
-    // Tiles 0 .. NS - 2 have landed (the full wait above); stage NS - 1 is
-    // filled by the first iteration.
+    // Tile 0 and the W1 rows have landed for every wave after this barrier
+    // (tiles 1 .. NS - 2 may still fly: the loop waits for each before
+    // reading it); stage NS - 1 is refilled by the first step.
     int st = 0;
     Scores S0, S1;
     block_barrier();
-    if (n > 0 && wave_on) score(0, S0);
-    for (int it = 0; it < n; it += 2) {
-        step_tile(it, st, S0, S1);
-        if (it + 1 < n) step_tile(it + 1, st, S1, S0);
+    if (wave_on) {
+#pragma unroll
+        for (int s = 0; s < RS; ++s) {
+            u[s] = ring[NS - 1][(nbw * RS + s) * 64 + lane];
+            if (s * 16 + lhalf * 8 >= r) u[s] = u32x4{0u, 0u, 0u, 0u};
+        }
+        score(0, S0);
+    }
+    step_tile(0, st, S0, S1, true);
+    for (int it = 1; it < n; it += 2) {
+        step_tile(it, st, S1, S0, false);
+        if (it + 1 < n) step_tile(it + 1, st, S0, S1, false);
     }
 
     // Merge: the lane pair that holds the same block, then the VW waves of
@@ -415,6 +451,7 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
         for (int i = 0; i < KL; ++i) topk_insert<KL>(list, other[i]);
     }
     u64* s_list = reinterpret_cast<u64*>(&ring[0][0]);  // [wave][32][KL]
+    wait_vmcnt<0>();   // with n == 1 the extra copies of the prologue may still fly
     __syncthreads();
     if (lhalf == 0) {
 #pragma unroll
