@@ -79,13 +79,16 @@ __device__ __forceinline__ float lane_select(float if_set, float if_clear, u64 l
 // Insert `key` into the descending list `list[0..K)`, keeping the K largest.
 template <int K>
 __device__ __forceinline__ void topk_insert(u64 (&list)[K], u64 key) {
+    // The list is in decreasing order, so key > list[i] implies key > list[i + 1]:
+    // all K comparisons are independent, and entry i becomes list[i - 1] (the
+    // key went above it), the key (it lands here) or stays. A key not above
+    // the last entry (0 among them) changes nothing.
+    bool gt[K];
 #pragma unroll
-    for (int i = 0; i < K; ++i) {
-        u64 hi = list[i] > key ? list[i] : key;
-        u64 lo = list[i] > key ? key : list[i];
-        list[i] = hi;
-        key = lo;
-    }
+    for (int i = 0; i < K; ++i) gt[i] = key > list[i];
+#pragma unroll
+    for (int i = K - 1; i > 0; --i) list[i] = gt[i - 1] ? list[i - 1] : (gt[i] ? key : list[i]);
+    list[0] = gt[0] ? key : list[0];
 }
 
 // ---- direct-to-LDS pipelines ----------------------------------------------

@@ -327,10 +327,7 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int v = vlane + 8 * (e >> 2) + (e & 3);
-                if (active && v < V) {
-                    const u64 key = make_key(z[e], v);
-                    if (key > list[KL - 1]) topk_insert<KL>(list, key);
-                }
+                topk_insert<KL>(list, (active && v < V) ? make_key(z[e], v) : 0ull);
             }
         } else if constexpr (KL == 1) {
             // Argmax of the lane's 16 columns: a strictly greater score moves
@@ -366,26 +363,26 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) hits |= (z[e] >= thr ? 1u : 0u) << e;
                 if (!active) hits = 0u;
+                // Every lane runs every round (no branch): a lane whose hits
+                // are done inserts the empty key 0, which changes nothing.
                 while (__any(hits != 0u)) {
-                    if (hits != 0u) {
-                        const int e = __builtin_ctz(hits);
-                        hits &= hits - 1u;
-                        // z[e] by a select tree on the bits of e
-                        const u64 m0 = __builtin_amdgcn_ballot_w64((e & 1) != 0);
-                        const u64 m1 = __builtin_amdgcn_ballot_w64((e & 2) != 0);
-                        const u64 m2 = __builtin_amdgcn_ballot_w64((e & 4) != 0);
-                        const u64 m3 = __builtin_amdgcn_ballot_w64((e & 8) != 0);
-                        float s8[8], s4[4], s2[2];
+                    const bool has = hits != 0u;
+                    const int e = __builtin_ctz(hits | 0x10000u);
+                    hits &= hits - 1u;
+                    // z[e] by a select tree on the bits of e
+                    const u64 m0 = __builtin_amdgcn_ballot_w64((e & 1) != 0);
+                    const u64 m1 = __builtin_amdgcn_ballot_w64((e & 2) != 0);
+                    const u64 m2 = __builtin_amdgcn_ballot_w64((e & 4) != 0);
+                    const u64 m3 = __builtin_amdgcn_ballot_w64((e & 8) != 0);
+                    float s8[8], s4[4], s2[2];
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) s8[i] = lane_select(z[2 * i + 1], z[2 * i], m0);
+                    for (int i = 0; i < 8; ++i) s8[i] = lane_select(z[2 * i + 1], z[2 * i], m0);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) s4[i] = lane_select(s8[2 * i + 1], s8[2 * i], m1);
+                    for (int i = 0; i < 4; ++i) s4[i] = lane_select(s8[2 * i + 1], s8[2 * i], m1);
 #pragma unroll
-                        for (int i = 0; i < 2; ++i) s2[i] = lane_select(s4[2 * i + 1], s4[2 * i], m2);
-                        const float ze = lane_select(s2[1], s2[0], m3);
-                        const u64 key = make_key(ze, vlane + 8 * (e >> 2) + (e & 3));
-                        if (key > list[KL - 1]) topk_insert<KL>(list, key);
-                    }
+                    for (int i = 0; i < 2; ++i) s2[i] = lane_select(s4[2 * i + 1], s4[2 * i], m2);
+                    const float ze = lane_select(s2[1], s2[0], m3);
+                    topk_insert<KL>(list, has ? make_key(ze, vlane + 8 * (e >> 2) + (e & 3)) : 0ull);
                 }
             }
         }
@@ -529,10 +526,7 @@ __global__ __launch_bounds__(256) void chain_step_direct(ChainArgs a, int j) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int v = vq + e;
-                    if (v < V) {
-                        const u64 key = make_key(acc[4 * q + e], v);
-                        if (key > list[nb][KL - 1]) topk_insert<KL>(list[nb], key);
-                    }
+                    topk_insert<KL>(list[nb], v < V ? make_key(acc[4 * q + e], v) : 0ull);
                 }
             }
         }
@@ -622,8 +616,7 @@ __global__ __launch_bounds__(256) void finalize(FinalArgs a) {
         const u64* p = a.partials + ((long)j * B + b) * a.nwg * k;
         const int cnt = a.nwg * k;
         for (int e = threadIdx.x; e < cnt; e += 256) {
-            const u64 key = p[e];
-            if (key > list[KL - 1]) topk_insert<KL>(list, key);
+            topk_insert<KL>(list, p[e]);
         }
 #pragma unroll
         for (int mask = 32; mask >= 1; mask >>= 1) {
