@@ -344,15 +344,25 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
             const u64 key = make_key(best, vlane + 8 * (be >> 2) + (be & 3));
             if (active && key > list[0]) list[0] = key;
         } else {
-            // Filtered inserts: a score can only enter this lane's list if it
-            // reaches the list's last entry, and cannot be among the block's
-            // best KL if it is below the last entry of the partner lane's
-            // list or of the other waves' lists for the same blocks (every
-            // such list holds KL scores of the block). A score equal to the
+            // Filtered inserts: a score cannot be among the block's best KL
+            // if KL other columns of the block score above it. The bound is
+            // the KL-th best of the union of this lane's list and the partner
+            // lane's (both decreasing: the largest over the splits of KL
+            // between them of the smaller of the two entries that close the
+            // split), published for the other waves of the block group, and
+            // raised to their last published bounds. A score equal to the
             // bound passes, so the full key comparison settles ties by
             // column. Hits are inserted in rounds, one per lane per round.
-            float thr = list[KL - 1] != 0ull ? key_score(list[KL - 1]) : -INFINITY;
-            thr = fmaxf(thr, __shfl_xor(thr, 32, kWave));
+            float sa[KL], sb[KL];
+#pragma unroll
+            for (int i = 0; i < KL; ++i) {
+                sa[i] = list[i] != 0ull ? key_score(list[i]) : -INFINITY;
+                sb[i] = __shfl_xor(sa[i], 32, kWave);
+            }
+            float thr = fmaxf(sa[KL - 1], sb[KL - 1]);
+#pragma unroll
+            for (int i = 1; i < KL; ++i) thr = fmaxf(thr, fminf(sa[i - 1], sb[KL - 1 - i]));
+            if (lhalf == 0) s_thr[wave][lrow] = thr;
 #pragma unroll
             for (int w = 0; w < VW; ++w) thr = fmaxf(thr, s_thr[nbw * VW + w][lrow]);
             float zmax = z[0];
@@ -385,12 +395,6 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
                     topk_insert<KL>(list, has ? make_key(ze, vlane + 8 * (e >> 2) + (e & 3)) : 0ull);
                 }
             }
-        }
-        if (KL > 1) {
-            // publish this wave's bound for the partner wave's next tile
-            float own = list[KL - 1] != 0ull ? key_score(list[KL - 1]) : -INFINITY;
-            own = fmaxf(own, __shfl_xor(own, 32, kWave));
-            if (lhalf == 0) s_thr[wave][lrow] = own;
         }
     };
     // one iteration: bring tile it + 1 in and score it, then consume tile it.
