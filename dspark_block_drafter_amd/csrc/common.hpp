@@ -127,5 +127,7 @@ __device__ __forceinline__ void block_barrier() {
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef __attribute__((address_space(3))) char lds_char;
+// Cache policy of a load that is read once (non-temporal: gfx950 "nt").
+constexpr int kLoadNT = 2;
 
 }  // namespace dspark

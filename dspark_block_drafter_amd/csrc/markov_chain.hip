@@ -221,15 +221,22 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
     // lambdas, the host pass stops emitting this kernel's launch stub.)
     lds_char* ring_dma = (lds_char*)(lds_ptr)&ring[0][0];
     asm volatile("" : "+s"(ring_dma));
+    // Load i of a wave is a markov_w2 load for i < W_INST / kWaves, a logits
+    // load after. The logits are read once: those loads are non-temporal, so
+    // they do not push markov_w2 (read again by every slot) out of the caches.
+    static_assert(W_INST % kWaves == 0, "the first loads of every wave are the markov_w2 ones");
+    auto copy = [&](int i, const void* p, int st) __attribute__((always_inline)) {
+        lds_ptr d = (lds_ptr)(ring_dma + (st * STAGE + dst[i]) * 16);
+        if (i < W_INST / kWaves) __builtin_amdgcn_global_load_lds(p, d, 16, 0, 0);
+        else __builtin_amdgcn_global_load_lds(p, d, 16, 0, kLoadNT);
+    };
     // Columns past V: markov_w2 rows are clamped to row V-1, logits to the
     // last 16-byte chunk of the row; such columns are never scored.
     auto issue = [&](int st, int t) __attribute__((always_inline)) {
         const int v0 = t * TS;
         if (v0 + TS <= V) {   // whole tile inside the vocabulary: no clamping
 #pragma unroll
-            for (int i = 0; i < LW; ++i)
-                __builtin_amdgcn_global_load_lds((const void*)(src[i] + (long)t * step[i]),
-                                                 (lds_ptr)(ring_dma + (st * STAGE + dst[i]) * 16), 16, 0, 0);
+            for (int i = 0; i < LW; ++i) copy(i, src[i] + (long)t * step[i], st);
             return;
         }
 #pragma unroll
@@ -243,7 +250,7 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
                 const int c = (slot % LR) ^ swz_rows<LR>(slot / LR);
                 if (v0 + 4 * c > V - 4) p -= (long)(v0 + 4 * c - (V - 4)) * 4;
             }
-            __builtin_amdgcn_global_load_lds((const void*)p, (lds_ptr)(ring_dma + (st * STAGE + dst[i]) * 16), 16, 0, 0);
+            copy(i, p, st);
         }
     };
 
