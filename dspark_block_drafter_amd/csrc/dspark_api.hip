@@ -109,7 +109,7 @@ int run_chain(const float* logits, const void* hidden, int hidden_dtype, const u
     c.r = r;
     c.n_pred = n_pred;
     c.top_k = top_k;
-    c.nwg = chain_workgroups(B, V, r);
+    c.nwg = chain_workgroups(B, V, r, top_k);
 
     hipError_t e = launch_chain_init(c, stream);
     if (e == hipSuccess && x.p_min_b) {

@@ -19,19 +19,30 @@ struct GemmArgs {
 hipError_t launch_lmhead_gemm(const GemmArgs& a, bool hidden_f32, hipStream_t stream);
 
 // ---- Markov chain -----------------------------------------------------------
-// Chain step geometry. With V % 4 == 0 the pipelined kernel runs at most
-// kChainMaxWGs workgroups (one per CU), each streaming a contiguous range of
-// tiles of chain_tile(B, r) columns; otherwise the direct kernel runs one
-// workgroup per kChainTileV columns.
-constexpr int kChainMaxWGs = 256;
+// Chain step geometry. With V % 4 == 0 the pipelined kernel streams, per
+// workgroup, a contiguous range of tiles of chain_tile(B, r) columns. Its
+// two-stage form (chain_two_stage: the LDS ring is 64 KB or less) runs two
+// workgroups per CU, kChainMaxWGs of them; the three- and four-stage forms
+// one per CU, kChainCUs. Otherwise the direct kernel runs one workgroup per
+// kChainTileV columns.
+constexpr int kChainCUs = 256;
+constexpr int kChainMaxWGs = 2 * kChainCUs;
 constexpr int kChainTileV = 128;
 inline bool chain_pipelined(int V) { return (V & 3) == 0; }
 inline int chain_tile(int B, int r) { return (B <= 32 && r <= 128) ? 128 : 64; }
-inline int chain_workgroups(int B, int V, int r) {
+// The two-stage form pays where the inserts of a top-k list are the larger
+// part of a tile (two block groups, top_k > 1): a second workgroup per CU
+// overlaps them. A top-1 step or a single block group streams better with
+// the deeper ring and one workgroup per CU.
+inline bool chain_two_stage(int B, int r, int top_k) {
+    return B > 32 && top_k > 1 && (r + 15) / 16 <= 8;
+}
+inline int chain_workgroups(int B, int V, int r, int top_k) {
     if (chain_pipelined(V)) {
         const int ts = chain_tile(B, r);
         const int nt = (V + ts - 1) / ts;
-        return nt < kChainMaxWGs ? nt : kChainMaxWGs;
+        const int cap = chain_two_stage(B, r, top_k) ? kChainMaxWGs : kChainCUs;
+        return nt < cap ? nt : cap;
     }
     return (V + kChainTileV - 1) / kChainTileV;
 }
@@ -44,7 +55,6 @@ inline int chain_workgroups_max(int V) {
     }
     return (V + kChainTileV - 1) / kChainTileV;
 }
-
 // Flags word bits (the public values of DSPARK_FLAG_*).
 constexpr uint32_t kFlagBadAnchor = 1u, kFlagInternal = 2u, kFlagBadD2t = 4u;
 

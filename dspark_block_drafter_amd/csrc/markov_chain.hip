@@ -269,7 +269,7 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
     // copy of the last tile, which no iteration reads. Lanes of blocks past B
     // read row 0 (their scores are never inserted); chunks past the rank are
     // zeroed when read.
-    static_assert(NS >= 3, "the first step waits for tile 1 with NS - 3 stages newer");
+    static_assert(NS >= 2, "a stage in use and one in flight at least");
     static_assert(NB * RS * 64 <= STAGE, "W1 rows fit stage NS - 1");
     issue(0, t0);
     if (RS > 0 && vb == 0 && nbw < NB) {
@@ -412,7 +412,7 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
         const int nst = st + 1 == NS ? 0 : st + 1;
         if (it + 1 < n) {
             if (first) {
-                wait_vmcnt<(NS - 3) * LW>();
+                wait_vmcnt<(NS >= 3 ? (NS - 3) * LW : 0)>();
             } else {
                 if (it + NS - 1 < n) issue((st + NS - 1) % NS, t0 + it + NS - 1);
                 wait_stages<LW, NS - 2>(min(NS - 2, n - 2 - it));
@@ -443,10 +443,34 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
         }
         score(0, S0);
     }
-    step_tile(0, st, S0, S1, true);
-    for (int it = 1; it < n; it += 2) {
-        step_tile(it, st, S1, S0, false);
-        if (it + 1 < n) step_tile(it + 1, st, S0, S1, false);
+    if constexpr (NS >= 3) {
+        step_tile(0, st, S0, S1, true);
+        for (int it = 1; it < n; it += 2) {
+            step_tile(it, st, S1, S0, false);
+            if (it + 1 < n) step_tile(it + 1, st, S0, S1, false);
+        }
+    } else {
+        // Two stages (two workgroups per CU): tile t sits in stage t & 1.
+        // Tile it + 1 is loaded while the wave inserts tile it; it goes to
+        // the stage of tile it - 1, which every wave finished reading before
+        // the previous barrier. Stage 1 first held the W1 rows: every wave
+        // has read them before this barrier.
+        wait_lds_reads();
+        block_barrier();
+        auto step2 = [&](int it, const Scores& cur, Scores& nxt) __attribute__((always_inline)) {
+            if (it + 1 < n) issue((it + 1) & 1, t0 + it + 1);
+            if (wave_on) consume(it, cur);
+            if (it + 1 < n) {
+                wait_vmcnt<0>();
+                wait_lds_reads();
+                block_barrier();
+                if (wave_on) score((it + 1) & 1, nxt);
+            }
+        };
+        for (int it = 0; it < n; it += 2) {
+            step2(it, S0, S1);
+            if (it + 1 < n) step2(it + 1, S1, S0);
+        }
     }
 
     // Merge: the lane pair that holds the same block, then the VW waves of
@@ -719,6 +743,9 @@ hipError_t step_pipe(const ChainArgs& a, int j, dim3 grid, hipStream_t s) {
     const int rs = (a.r + 15) / 16;
 #define DSPARK_STEP(RSV, NSV, VWV) \
     hipLaunchKernelGGL((chain_step_pipe<NB, KL, RSV, NSV, VWV>), grid, dim3(256), 0, s, a, j);
+    // Two stages for two block groups with top-k lists (two workgroups per
+    // CU, as chain_two_stage and chain_workgroups count them); otherwise
+    // four (three for the widest rings) and one workgroup per CU.
     if constexpr (NB == 1) {
         // one block group: all four waves take their own 32 columns
         if (rs == 0) { DSPARK_STEP(0, 4, 4) }
@@ -726,11 +753,17 @@ hipError_t step_pipe(const ChainArgs& a, int j, dim3 grid, hipStream_t s) {
         else if (rs <= 4) { DSPARK_STEP(4, 4, 4) }
         else if (rs <= 8) { DSPARK_STEP(8, 3, 4) }
         else { DSPARK_STEP(16, 3, 2) }
-    } else {
+    } else if constexpr (KL == 1) {
         if (rs == 0) { DSPARK_STEP(0, 4, 2) }
         else if (rs <= 2) { DSPARK_STEP(2, 4, 2) }
         else if (rs <= 4) { DSPARK_STEP(4, 4, 2) }
         else if (rs <= 8) { DSPARK_STEP(8, 4, 2) }
+        else { DSPARK_STEP(16, 3, 2) }
+    } else {
+        if (rs == 0) { DSPARK_STEP(0, 2, 2) }
+        else if (rs <= 2) { DSPARK_STEP(2, 2, 2) }
+        else if (rs <= 4) { DSPARK_STEP(4, 2, 2) }
+        else if (rs <= 8) { DSPARK_STEP(8, 2, 2) }
         else { DSPARK_STEP(16, 3, 2) }
     }
 #undef DSPARK_STEP

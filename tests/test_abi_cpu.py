@@ -45,9 +45,9 @@ def test_workspace_bytes_layout(lib):
     for B, L, V, k, lay in [(64, 16, 248320, 4, 0), (1, 16, 151936, 1, 0), (4, 7, 262144, 1, 1),
                             (3, 5, 1000, 3, 0), (5, 7, 777, 16, 1)]:
         n = L - lay
-        # chain workgroups: pipelined kernel (V % 4 == 0) runs min(ceil(V/64), 256),
-        # the direct kernel one per 128 columns
-        nwg = min((V + 63) // 64, 256) if V % 4 == 0 else (V + 127) // 128
+        # chain workgroups: pipelined kernel (V % 4 == 0) runs at most min(ceil(V/64), 512)
+        # (two per CU in its two-stage form), the direct kernel one per 128 columns
+        nwg = min((V + 63) // 64, 512) if V % 4 == 0 else (V + 127) // 128
         want = 256 + al(n * B * 8) + (al(n * B * nwg * k * 8) if k > 1 else 0)
         assert lib.dspark_workspace_bytes(B, L, V, k, lay) == want
 
