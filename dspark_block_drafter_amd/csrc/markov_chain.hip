@@ -575,29 +575,43 @@ __global__ __launch_bounds__(256) void chain_step_direct(ChainArgs a, int j) {
 // fp32 hidden rounded to bf16 first.
 __device__ __forceinline__ float slot_conf(const void* hidden, int hidden_f32, const uint16_t* conf_w,
                                            long row, int H, int lane) {
+    // Lane l sums h = 8l + 512i .. + 8 for i = 0, 1, ... in that order. The
+    // loads of four such chunks go out together (a chunk past H reads the
+    // lane's first chunk again and adds nothing).
+    constexpr int U = 4;
     float s = 0.0f;
-    for (int h = lane * 8; h < H; h += 64 * 8) {
-        const u32x4 cw = *reinterpret_cast<const u32x4*>(conf_w + h);
-        float x[8];
-        if (hidden_f32) {
-            const f32x4* hp = reinterpret_cast<const f32x4*>(static_cast<const float*>(hidden) + row * H + h);
-            const f32x4 x0 = hp[0], x1 = hp[1];
-            const uint32_t p0 = pack_bf16x2(x0[0], x0[1]), p1 = pack_bf16x2(x0[2], x0[3]);
-            const uint32_t p2 = pack_bf16x2(x1[0], x1[1]), p3 = pack_bf16x2(x1[2], x1[3]);
-            x[0] = bf16_lo(p0); x[1] = bf16_hi(p0); x[2] = bf16_lo(p1); x[3] = bf16_hi(p1);
-            x[4] = bf16_lo(p2); x[5] = bf16_hi(p2); x[6] = bf16_lo(p3); x[7] = bf16_hi(p3);
-        } else {
-            const u32x4 hv = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(hidden) + row * H + h);
+    for (int h0 = lane * 8; h0 < H; h0 += 64 * 8 * U) {
+        u32x4 cw[U];
+        float x[U][8];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                x[2 * q] = bf16_lo(hv[q]);
-                x[2 * q + 1] = bf16_hi(hv[q]);
+        for (int u = 0; u < U; ++u) {
+            const int h = h0 + u * 64 * 8 < H ? h0 + u * 64 * 8 : lane * 8;
+            cw[u] = *reinterpret_cast<const u32x4*>(conf_w + h);
+            if (hidden_f32) {
+                const f32x4* hp = reinterpret_cast<const f32x4*>(static_cast<const float*>(hidden) + row * H + h);
+                const f32x4 x0 = hp[0], x1 = hp[1];
+                const uint32_t p0 = pack_bf16x2(x0[0], x0[1]), p1 = pack_bf16x2(x0[2], x0[3]);
+                const uint32_t p2 = pack_bf16x2(x1[0], x1[1]), p3 = pack_bf16x2(x1[2], x1[3]);
+                x[u][0] = bf16_lo(p0); x[u][1] = bf16_hi(p0); x[u][2] = bf16_lo(p1); x[u][3] = bf16_hi(p1);
+                x[u][4] = bf16_lo(p2); x[u][5] = bf16_hi(p2); x[u][6] = bf16_lo(p3); x[u][7] = bf16_hi(p3);
+            } else {
+                const u32x4 hv =
+                    *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(hidden) + row * H + h);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    x[u][2 * q] = bf16_lo(hv[q]);
+                    x[u][2 * q + 1] = bf16_hi(hv[q]);
+                }
             }
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            s += x[2 * q] * bf16_lo(cw[q]);
-            s += x[2 * q + 1] * bf16_hi(cw[q]);
+        for (int u = 0; u < U; ++u) {
+            if (h0 + u * 64 * 8 >= H) break;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                s += x[u][2 * q] * bf16_lo(cw[u][q]);
+                s += x[u][2 * q + 1] * bf16_hi(cw[u][q]);
+            }
         }
     }
 #pragma unroll
@@ -650,8 +664,13 @@ __global__ __launch_bounds__(256) void finalize(FinalArgs a) {
         for (int i = 0; i < KL; ++i) list[i] = 0ull;
         const u64* p = a.partials + ((long)j * B + b) * a.nwg * k;
         const int cnt = a.nwg * k;
-        for (int e = threadIdx.x; e < cnt; e += 256) {
-            topk_insert<KL>(list, p[e]);
+        // eight independent loads at a time, then their inserts
+        for (int e0 = threadIdx.x; e0 < cnt; e0 += 256 * 8) {
+            u64 kk[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) kk[u] = e0 + u * 256 < cnt ? p[e0 + u * 256] : 0ull;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) topk_insert<KL>(list, kk[u]);
         }
 #pragma unroll
         for (int mask = 32; mask >= 1; mask >>= 1) {
