@@ -63,6 +63,14 @@ SMALL = {
     # several K steps; two K steps (loads past the end are clamped)
     "w4_ragged_K320": lambda: make_small(37, 8, 320, 3000, 16, top_k=2, conf=True, p_min=0.4, seed=21),
     "w4_two_ksteps": lambda: make_small(33, 9, 128, 1000, 8, top_k=1, layout=BONUS_ANCHOR, seed=22),
+    # several tiles per workgroup (V > 256 tiles): the two-stage ring of
+    # top-k over two block groups (2-3 tiles each of 512 workgroups), the
+    # four-stage ring with fewer tiles than stages (2-3 of 256) and with more
+    # (4-5 of 256, two block groups, top-1)
+    "two_stage_multi_tile": lambda: make_small(40, 4, 64, 70000, 64, top_k=4, seed=23),
+    "four_stage_short": lambda: make_small(4, 5, 64, 70000, 64, top_k=1, conf=True, p_min=0.45,
+                                           seed=24),
+    "four_stage_two_groups": lambda: make_small(34, 3, 64, 70000, 32, top_k=1, seed=25),
     "reduced_vocab": lambda: make_small(4, 7, 176, 4096, 64, top_k=4, layout=BONUS_ANCHOR,
                                         reachable=300, conf=True, p_min=0.5, conf_trend=True,
                                         seed=10),
