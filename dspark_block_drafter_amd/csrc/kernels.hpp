@@ -19,32 +19,38 @@ struct GemmArgs {
 hipError_t launch_lmhead_gemm(const GemmArgs& a, bool hidden_f32, hipStream_t stream);
 
 // ---- Markov chain -----------------------------------------------------------
-// Chain step geometry. With V % 4 == 0 the pipelined kernel streams, per
-// workgroup, a contiguous range of tiles of chain_tile(B, r) columns. Its
-// two-stage form (chain_two_stage: the LDS ring is 64 KB or less) runs two
-// workgroups per CU, kChainMaxWGs of them; the three- and four-stage forms
-// one per CU, kChainCUs. Otherwise the direct kernel runs one workgroup per
-// kChainTileV columns.
+// Chain step geometry. With V % 4 == 0 a workgroup streams a contiguous range
+// of tiles of chain_tile(B, r) columns in one of three forms:
+//  * kChainWave: every wave streams its own run of 32-column steps for its
+//    own 32 blocks through a private LDS ring, with no workgroup barrier
+//    inside the loop; one workgroup per CU (kChainCUs). Rank up to 128.
+//  * kChainPipeTwo: one shared two-stage ring per workgroup, two workgroups
+//    per CU (kChainMaxWGs).
+//  * kChainPipeDeep: one shared three- or four-stage ring, one workgroup per CU.
+// Otherwise (V % 4 != 0) the direct kernel runs one workgroup per kChainTileV
+// columns. The per-wave form is the faster one for top-1 steps and for one
+// block group (8-12% at the Gemma-4 and Qwen3-8B shapes, 3% on the B = 8 top-4
+// tree). Top-k lists over two block groups stay on the two-per-CU ring: there
+// a wave's inserts are the larger part of a step, and the second workgroup
+// on the CU hides them (493 against 533 us per call at B = 64).
 constexpr int kChainCUs = 256;
 constexpr int kChainMaxWGs = 2 * kChainCUs;
 constexpr int kChainTileV = 128;
+enum ChainForm { kChainDirect, kChainWave, kChainPipeTwo, kChainPipeDeep };
 inline bool chain_pipelined(int V) { return (V & 3) == 0; }
 inline int chain_tile(int B, int r) { return (B <= 32 && r <= 128) ? 128 : 64; }
-// The two-stage form pays where the inserts of a top-k list are the larger
-// part of a tile (two block groups, top_k > 1): a second workgroup per CU
-// overlaps them. A top-1 step or a single block group streams better with
-// the deeper ring and one workgroup per CU.
-inline bool chain_two_stage(int B, int r, int top_k) {
-    return B > 32 && top_k > 1 && (r + 15) / 16 <= 8;
+inline ChainForm chain_form(int B, int V, int r, int top_k) {
+    if (!chain_pipelined(V)) return kChainDirect;
+    if ((r + 15) / 16 > 8) return kChainPipeDeep;
+    return (B > 32 && top_k > 1) ? kChainPipeTwo : kChainWave;
 }
 inline int chain_workgroups(int B, int V, int r, int top_k) {
-    if (chain_pipelined(V)) {
-        const int ts = chain_tile(B, r);
-        const int nt = (V + ts - 1) / ts;
-        const int cap = chain_two_stage(B, r, top_k) ? kChainMaxWGs : kChainCUs;
-        return nt < cap ? nt : cap;
-    }
-    return (V + kChainTileV - 1) / kChainTileV;
+    const ChainForm f = chain_form(B, V, r, top_k);
+    if (f == kChainDirect) return (V + kChainTileV - 1) / kChainTileV;
+    const int ts = chain_tile(B, r);
+    const int nt = (V + ts - 1) / ts;
+    const int cap = f == kChainPipeTwo ? kChainMaxWGs : kChainCUs;
+    return nt < cap ? nt : cap;
 }
 // Upper bound of chain_workgroups over every rank (workspace sizing does not
 // know r): the narrowest tile gives the most workgroups.

@@ -506,6 +506,333 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
     }
 }
 
+// ---- step kernel for V % 4 == 0: a private ring per wave ----------------------
+
+// Wave w of workgroup g scores the 32-column block w % VW of every tile in
+// the workgroup's range [t0, t1) (TS = 32 VW columns per tile) for the block
+// group w / VW (VW = 2 for two groups of 32 blocks, 4 for one group). Each
+// wave streams its own markov_w2 rows and slot-j logits rows through its own
+// NS-stage LDS ring of direct-to-LDS copies, so its loop needs no workgroup
+// barrier: a slow insert round holds up only that wave, and all NS stages are
+// in flight while it inserts (a stage is refilled as soon as its tile has
+// been read into the accumulators). With two block groups the two waves of a
+// column block both copy its markov_w2 rows (the second copy is an L2 hit).
+// The waves that score the same blocks share their top-k bounds through LDS
+// without synchronisation: every published value is a valid bound whenever
+// it is read. The workgroup merges and publishes once per slot.
+template <int NB, int KL, int RS, int NS>
+__global__ __launch_bounds__(256) void chain_step_wave(ChainArgs a, int j) {
+    constexpr int VW = kWaves / NB;         // 32-column blocks per tile
+    constexpr int TS = 32 * VW;             // columns per tile
+    constexpr int WR = 2 * RS;              // 16-byte chunks per staged markov_w2 row
+    constexpr int WRd = WR > 0 ? WR : 1;
+    constexpr int LR = 8;                   // 16-byte chunks per staged logits row (32 columns)
+    constexpr int W_SLOTS = 32 * WR;
+    constexpr int L_SLOTS = 32 * LR;
+    constexpr int STAGE = W_SLOTS + L_SLOTS;
+    constexpr int W_INST = W_SLOTS / 64, L_INST = L_SLOTS / 64;
+    constexpr int LW = W_INST + L_INST;     // copies per tile per wave
+    static_assert(NB == 1 || NB == 2, "one or two block groups");
+    static_assert(NS >= 2 && NS * LW + RS < 64, "vmcnt range");
+    static_assert(RS * 64 <= STAGE, "W1 rows fit one stage");
+    static_assert(KL * 32 * 8 <= STAGE * 16, "list merge reuses a wave's ring");
+    __shared__ u32x4 ring[kWaves][NS][STAGE];
+    // Top-k bound of each wave's lane pairs, per block (see consume below).
+    __shared__ float s_thr[kWaves][32];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int lrow = lane & 31, lhalf = lane >> 5;
+    const int vb = wave % VW, nbw = wave / VW;
+    if (a.stop && j >= *a.stop) return;   // adaptive gate: every block was cut
+    const int bbase = blockIdx.y * NB * 32;
+    const int B = a.B, V = a.V, r = a.r;
+    const int nT = (V + TS - 1) / TS, G = gridDim.x, g = blockIdx.x;
+    const int t0 = (int)((long)nT * g / G), t1 = (int)((long)nT * (g + 1) / G);
+    const int n = t1 - t0;                  // >= 1: there are at most as many workgroups as tiles
+
+    // The workgroup's columns [t0 TS, t1 TS) are cut into VW contiguous runs
+    // of n 32-column steps, one per column block: wave vb streams columns
+    // cbase + 32 it, it = 0 .. n-1, so each wave reads its markov_w2 and
+    // logits rows front to back.
+    const int cbase = (t0 * VW + vb * n) * 32;
+    // This lane's fixed part of each of its LW copies per step (step 0).
+    const char* src[LW];
+    int dst[LW];
+#pragma unroll
+    for (int i = 0; i < LW; ++i) {
+        if (i < W_INST) {
+            const int slot = i * 64 + lane, row = slot / WRd;
+            const int c = (slot % WRd) ^ swz_rows<WR>(row);
+            const int k = c * 8 < r ? c * 8 : 0;   // rank padding: any valid chunk
+            src[i] = reinterpret_cast<const char*>(a.w2 + (long)(cbase + row) * r + k);
+        } else {
+            const int slot = (i - W_INST) * 64 + lane, row = slot / LR;
+            const int c = (slot % LR) ^ swz_rows<LR>(row);
+            const int b = min(bbase + nbw * 32 + row, B - 1);
+            src[i] = reinterpret_cast<const char*>(a.logits + ((long)b * a.n_pred + j) * V + cbase + 4 * c);
+        }
+        dst[i] = i * 64;
+    }
+    // Copies address the ring through a base the compiler cannot trace to the
+    // array (as in chain_step_pipe): the explicit waits order the reads.
+    lds_char* ring_dma = (lds_char*)(lds_ptr)&ring[wave][0][0];
+    asm volatile("" : "+s"(ring_dma));
+    auto copy = [&](int i, const void* p, int st) __attribute__((always_inline)) {
+        lds_ptr d = (lds_ptr)(ring_dma + (st * STAGE + dst[i]) * 16);
+        if (i < W_INST) __builtin_amdgcn_global_load_lds(p, d, 16, 0, 0);
+        else __builtin_amdgcn_global_load_lds(p, d, 16, 0, kLoadNT);
+    };
+    // Columns past V: markov_w2 rows are clamped to row V-1, logits to the
+    // last 16-byte chunk of the row; such columns are never scored.
+    auto issue = [&](int st, int t) __attribute__((always_inline)) {
+        const int v0 = cbase + t * 32;
+        if (v0 + 32 <= V) {
+#pragma unroll
+            for (int i = 0; i < LW; ++i) copy(i, src[i] + (long)t * (i < W_INST ? 64 * r : 128), st);
+            return;
+        }
+#pragma unroll
+        for (int i = 0; i < LW; ++i) {
+            const char* p = src[i] + (long)t * (i < W_INST ? 64 * r : 128);
+            if (i < W_INST) {
+                const int row = (i * 64 + lane) / WRd;
+                if (v0 + row >= V) p -= (long)(v0 + row - (V - 1)) * r * 2;
+            } else {
+                const int slot = (i - W_INST) * 64 + lane;
+                const int c = (slot % LR) ^ swz_rows<LR>(slot / LR);
+                if (v0 + 4 * c > V - 4) p -= (long)(v0 + 4 * c - (V - 4)) * 4;
+            }
+            copy(i, p, st);
+        }
+    };
+
+    const int bme = bbase + nbw * 32 + lrow;
+    const bool active = bme < B;
+    const int prev = active ? prev_token(a, j, bme, vb == 0) : 0;
+    if (lhalf == 0) s_thr[wave][lrow] = -INFINITY;
+    wait_lds_reads();
+    block_barrier();   // every bound is set before any wave reads it
+
+    // Tile 0, the markov_w1 rows of prev (the MFMA B operand) into stage
+    // NS-1, tiles 1 .. NS-2; then, once tile 0 and the W1 rows have landed and
+    // the rows are in registers, tile NS-1 into stage NS-1. A stage past the
+    // last tile gets a second copy of it (no iteration reads it), so the
+    // number of copies in flight is fixed. Chunks past the rank are zeroed
+    // when read.
+    issue(0, 0);
+    if constexpr (RS > 0) {
+#pragma unroll
+        for (int s = 0; s < RS; ++s) {
+            const int k0 = s * 16 + lhalf * 8;
+            __builtin_amdgcn_global_load_lds((const void*)(a.w1 + (long)prev * r + (k0 < r ? k0 : 0)),
+                                             (lds_ptr)(ring_dma + ((NS - 1) * STAGE + s * 64) * 16), 16, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int t = 1; t < NS - 1; ++t) issue(t, min(t, n - 1));
+    wait_vmcnt<(NS - 2) * LW>();
+    asm volatile("" ::: "memory");
+    u32x4 u[RS > 0 ? RS : 1];
+#pragma unroll
+    for (int s = 0; s < RS; ++s) {
+        u[s] = ring[wave][NS - 1][s * 64 + lane];
+        if (s * 16 + lhalf * 8 >= r) u[s] = u32x4{0u, 0u, 0u, 0u};
+    }
+    asm volatile("" ::: "memory");
+    wait_lds_reads();
+    asm volatile("" ::: "memory");
+    issue(NS - 1, min(NS - 1, n - 1));
+
+    u64 list[KL];
+#pragma unroll
+    for (int i = 0; i < KL; ++i) list[i] = 0ull;
+    // (an LDS-qualified pointer: a generic one would become a flat load,
+    // which waits for every copy in flight)
+    typedef const volatile __attribute__((address_space(3))) float lds_vfloat;
+    lds_vfloat* thr_v = (lds_vfloat*)&s_thr[0][0];
+
+    // The slot-j logits of a tile enter the MFMA as its accumulator input,
+    // so the accumulator ends as the biased score z = logits + W2 . W1[prev].
+    auto score = [&](int st_, f32x16& acc) __attribute__((always_inline)) {
+        const u32x4* stg = ring[wave][st_];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int c = 2 * q + lhalf;
+            const f32x4 x = __builtin_bit_cast(f32x4, stg[W_SLOTS + lrow * LR + (c ^ swz_rows<LR>(lrow))]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[4 * q + e] = x[e];
+        }
+#pragma unroll
+        for (int s = 0; s < RS; ++s) {
+            const u32x4 w = stg[lrow * WR + ((2 * s + lhalf) ^ swz_rows<WR>(lrow))];
+            acc = mfma32x32x16(w, u[s], acc);
+        }
+    };
+    auto consume = [&](int it, const f32x16& acc) __attribute__((always_inline)) {
+        const int vt = cbase + it * 32;
+        // acc[4q + e] is the biased score of column vt + 8q + 4(lane/32) + e;
+        // the column rises with the index.
+        float z[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) z[e] = acc[e];
+        const int vlane = vt + 4 * lhalf;
+        if (vt + 32 > V) {
+            // the ragged last tile: plain inserts of the columns inside V
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int v = vlane + 8 * (e >> 2) + (e & 3);
+                topk_insert<KL>(list, (active && v < V) ? make_key(z[e], v) : 0ull);
+            }
+        } else if constexpr (KL == 1) {
+            // Argmax of the lane's 16 columns: a strictly greater score moves
+            // the pick, so equal scores keep the lower column.
+            float best = z[0];
+            int be = 0;
+#pragma unroll
+            for (int e = 1; e < 16; ++e) {
+                const bool gt = z[e] > best;
+                best = gt ? z[e] : best;
+                be = gt ? e : be;
+            }
+            const u64 key = make_key(best, vlane + 8 * (be >> 2) + (be & 3));
+            if (active && key > list[0]) list[0] = key;
+        } else {
+            // Filtered inserts. A score below a bound that KL distinct
+            // columns of the block reach cannot be among its best KL. Bounds:
+            // the KL-th best of the union of this lane's list and the partner
+            // lane's (both decreasing: the largest over the splits of KL
+            // between them of the smaller of the two closing entries); on the
+            // wave's first tile, when the lists are still short, the smallest
+            // of KL maxima over disjoint groups of the tile's 16 / KL columns,
+            // from either lane of the pair; and the bounds the other waves of
+            // the block group last published. A score equal to the bound
+            // passes, so the full key comparison settles ties by column. Hits
+            // are inserted in rounds, one per lane per round.
+            float sa[KL], sb[KL];
+#pragma unroll
+            for (int i = 0; i < KL; ++i) {
+                sa[i] = list[i] != 0ull ? key_score(list[i]) : -INFINITY;
+                sb[i] = __shfl_xor(sa[i], 32, kWave);
+            }
+            float thr = fmaxf(sa[KL - 1], sb[KL - 1]);
+#pragma unroll
+            for (int i = 1; i < KL; ++i) thr = fmaxf(thr, fminf(sa[i - 1], sb[KL - 1 - i]));
+            if (it == 0) {
+                constexpr int GS = 16 / KL;
+                static_assert(GS * KL == 16, "KL divides 16");
+                float tb = INFINITY;
+#pragma unroll
+                for (int gi = 0; gi < KL; ++gi) {
+                    float m = z[gi * GS];
+#pragma unroll
+                    for (int e = 1; e < GS; ++e) m = fmaxf(m, z[gi * GS + e]);
+                    tb = fminf(tb, m);
+                }
+                tb = fmaxf(tb, __shfl_xor(tb, 32, kWave));
+                thr = fmaxf(thr, tb);
+            }
+            if (lhalf == 0 && active) s_thr[wave][lrow] = thr;
+#pragma unroll
+            for (int w = 0; w < VW; ++w)
+                if (w != vb) thr = fmaxf(thr, thr_v[(nbw * VW + w) * 32 + lrow]);
+            float zmax = z[0];
+#pragma unroll
+            for (int e = 1; e < 16; ++e) zmax = fmaxf(zmax, z[e]);
+            if (__any(active && zmax >= thr)) {
+                unsigned hits = 0u;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) hits |= (z[e] >= thr ? 1u : 0u) << e;
+                if (!active) hits = 0u;
+                // Every lane runs every round (no branch): a lane whose hits
+                // are done inserts the empty key 0, which changes nothing.
+                while (__any(hits != 0u)) {
+                    const bool has = hits != 0u;
+                    const int e = __builtin_ctz(hits | 0x10000u);
+                    hits &= hits - 1u;
+                    // z[e] by a select tree on the bits of e
+                    const u64 m0 = __builtin_amdgcn_ballot_w64((e & 1) != 0);
+                    const u64 m1 = __builtin_amdgcn_ballot_w64((e & 2) != 0);
+                    const u64 m2 = __builtin_amdgcn_ballot_w64((e & 4) != 0);
+                    const u64 m3 = __builtin_amdgcn_ballot_w64((e & 8) != 0);
+                    float s8[8], s4[4], s2[2];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) s8[i] = lane_select(z[2 * i + 1], z[2 * i], m0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) s4[i] = lane_select(s8[2 * i + 1], s8[2 * i], m1);
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) s2[i] = lane_select(s4[2 * i + 1], s4[2 * i], m2);
+                    const float ze = lane_select(s2[1], s2[0], m3);
+                    topk_insert<KL>(list, has ? make_key(ze, vlane + 8 * (e >> 2) + (e & 3)) : 0ull);
+                }
+            }
+        }
+    };
+    // One iteration: the stage of tile it (already read into `cur`) is
+    // refilled with tile it + NS, tile it + 1 is waited for and scored, then
+    // tile it is consumed, so the matrix pipe and every stage's copy run while
+    // the wave inserts.
+    auto step_tile = [&](int it, int& st, const f32x16& cur, f32x16& nxt) __attribute__((always_inline)) {
+        if (it + NS < n) {
+            wait_lds_reads();
+            asm volatile("" ::: "memory");
+            issue(st, it + NS);
+        }
+        const int nst = st + 1 == NS ? 0 : st + 1;
+        if (it + 1 < n) {
+            // copies issued after tile it + 1: the prologue's NS tiles (with
+            // copies of the last tile when n < NS), then one per iteration
+            const int newer = n >= NS ? min(NS - 1, n - 2 - it) : NS - 2 - it;
+            wait_stages<LW, NS - 1>(newer);
+            asm volatile("" ::: "memory");
+            score(nst, nxt);
+        }
+        consume(it, cur);
+        st = nst;
+    };
+    int st = 0;
+    f32x16 S0, S1;
+    score(0, S0);
+    for (int it = 0; it < n; it += 2) {
+        step_tile(it, st, S0, S1);
+        if (it + 1 < n) step_tile(it + 1, st, S1, S0);
+    }
+
+    // Merge: the lane pair that holds the same block, then the VW waves of
+    // the block group through LDS (each wave's list in its own ring, whose
+    // copies have all landed).
+    {
+        u64 other[KL];
+#pragma unroll
+        for (int i = 0; i < KL; ++i) other[i] = shfl_xor_u64(list[i], 32);
+#pragma unroll
+        for (int i = 0; i < KL; ++i) topk_insert<KL>(list, other[i]);
+    }
+    wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
+    if (lhalf == 0) {
+        u64* s_list = reinterpret_cast<u64*>(&ring[wave][0][0]);
+#pragma unroll
+        for (int i = 0; i < KL; ++i) s_list[lrow * KL + i] = list[i];
+    }
+    __syncthreads();
+    if (vb == 0 && lhalf == 0 && active) {
+#pragma unroll
+        for (int w = 1; w < VW; ++w) {
+            const u64* o = reinterpret_cast<const u64*>(&ring[wave + w][0][0]);
+#pragma unroll
+            for (int i = 0; i < KL; ++i) topk_insert<KL>(list, o[lrow * KL + i]);
+        }
+        if (a.top_k > 1) {
+            u64* p = a.partials + (((long)j * B + bme) * a.nwg + g) * a.top_k;
+#pragma unroll
+            for (int i = 0; i < KL; ++i)
+                if (i < a.top_k) p[i] = list[i];
+        }
+        if (list[0] != 0ull) atomicMax(a.winners + (long)j * B + bme, list[0]);
+    }
+}
+
 // ---- step kernel for any V: operands read straight from global memory --------
 
 template <int NB, int KL, int RS>
@@ -758,49 +1085,65 @@ hipError_t step_direct(const ChainArgs& a, int j, dim3 grid, hipStream_t s) {
 }
 
 template <int NB, int KL>
-hipError_t step_pipe(const ChainArgs& a, int j, dim3 grid, hipStream_t s) {
+hipError_t step_pipe(const ChainArgs& a, int j, dim3 grid, bool two, hipStream_t s) {
     const int rs = (a.r + 15) / 16;
 #define DSPARK_STEP(RSV, NSV, VWV) \
     hipLaunchKernelGGL((chain_step_pipe<NB, KL, RSV, NSV, VWV>), grid, dim3(256), 0, s, a, j);
-    // Two stages for two block groups with top-k lists (two workgroups per
-    // CU, as chain_two_stage and chain_workgroups count them); otherwise
-    // four (three for the widest rings) and one workgroup per CU.
-    if constexpr (NB == 1) {
-        // one block group: all four waves take their own 32 columns
-        if (rs == 0) { DSPARK_STEP(0, 4, 4) }
-        else if (rs <= 2) { DSPARK_STEP(2, 4, 4) }
-        else if (rs <= 4) { DSPARK_STEP(4, 4, 4) }
-        else if (rs <= 8) { DSPARK_STEP(8, 3, 4) }
-        else { DSPARK_STEP(16, 3, 2) }
-    } else if constexpr (KL == 1) {
-        if (rs == 0) { DSPARK_STEP(0, 4, 2) }
-        else if (rs <= 2) { DSPARK_STEP(2, 4, 2) }
-        else if (rs <= 4) { DSPARK_STEP(4, 4, 2) }
-        else if (rs <= 8) { DSPARK_STEP(8, 4, 2) }
-        else { DSPARK_STEP(16, 3, 2) }
+    // Two stages and two workgroups per CU (kChainPipeTwo: top-k lists over
+    // two block groups, rank up to 128); three stages, one workgroup per CU,
+    // for the widest rank (kChainPipeDeep).
+    if (two) {
+        if constexpr (NB == 2) {
+            if (rs == 0) { DSPARK_STEP(0, 2, 2) }
+            else if (rs <= 2) { DSPARK_STEP(2, 2, 2) }
+            else if (rs <= 4) { DSPARK_STEP(4, 2, 2) }
+            else if (rs <= 8) { DSPARK_STEP(8, 2, 2) }
+            else return hipErrorInvalidValue;   // chain_form never picks this form for it
+        } else {
+            return hipErrorInvalidValue;
+        }
     } else {
-        if (rs == 0) { DSPARK_STEP(0, 2, 2) }
-        else if (rs <= 2) { DSPARK_STEP(2, 2, 2) }
-        else if (rs <= 4) { DSPARK_STEP(4, 2, 2) }
-        else if (rs <= 8) { DSPARK_STEP(8, 2, 2) }
-        else { DSPARK_STEP(16, 3, 2) }
+        if (rs > 8) { DSPARK_STEP(16, 3, 2) }
+        else return hipErrorInvalidValue;   // narrower ranks take the other forms
     }
 #undef DSPARK_STEP
     return hipGetLastError();
 }
 
-template <int NB>
-hipError_t step_kl(const ChainArgs& a, int j, dim3 grid, bool pipe, hipStream_t s) {
-    if (pipe) {
-        if (a.top_k == 1) return step_pipe<NB, 1>(a, j, grid, s);
-        if (a.top_k <= 4) return step_pipe<NB, 4>(a, j, grid, s);
-        if (a.top_k <= 8) return step_pipe<NB, 8>(a, j, grid, s);
-        return step_pipe<NB, 16>(a, j, grid, s);
+// Per-wave rings: as many stages as fit 4 x NS x stage <= 159 KB (stage =
+// 32 markov_w2 rows of the rank plus 32 logits rows of 32 columns).
+template <int NB, int KL>
+hipError_t step_wave(const ChainArgs& a, int j, dim3 grid, hipStream_t s) {
+    const int rs = (a.r + 15) / 16;
+#define DSPARK_STEP(RSV, NSV) hipLaunchKernelGGL((chain_step_wave<NB, KL, RSV, NSV>), grid, dim3(256), 0, s, a, j);
+    if (rs == 0) { DSPARK_STEP(0, 8) }
+    else if (rs <= 2) { DSPARK_STEP(2, 6) }
+    else if (rs <= 4) { DSPARK_STEP(4, 4) }
+    else if (rs <= 8) { DSPARK_STEP(8, 3) }
+    else return hipErrorInvalidValue;   // chain_form never picks this form for a wider rank
+#undef DSPARK_STEP
+    return hipGetLastError();
+}
+
+template <int NB, int KL>
+hipError_t step_form(const ChainArgs& a, int j, dim3 grid, ChainForm f, hipStream_t s) {
+    switch (f) {
+        case kChainWave:
+            // (top-k lists over two block groups take the two-stage ring)
+            if constexpr (NB == 2 && KL > 1) return hipErrorInvalidValue;
+            else return step_wave<NB, KL>(a, j, grid, s);
+        case kChainPipeTwo: return step_pipe<NB, KL>(a, j, grid, true, s);
+        case kChainPipeDeep: return step_pipe<NB, KL>(a, j, grid, false, s);
+        default: return step_direct<NB, KL>(a, j, grid, s);
     }
-    if (a.top_k == 1) return step_direct<NB, 1>(a, j, grid, s);
-    if (a.top_k <= 4) return step_direct<NB, 4>(a, j, grid, s);
-    if (a.top_k <= 8) return step_direct<NB, 8>(a, j, grid, s);
-    return step_direct<NB, 16>(a, j, grid, s);
+}
+
+template <int NB>
+hipError_t step_kl(const ChainArgs& a, int j, dim3 grid, ChainForm f, hipStream_t s) {
+    if (a.top_k == 1) return step_form<NB, 1>(a, j, grid, f, s);
+    if (a.top_k <= 4) return step_form<NB, 4>(a, j, grid, f, s);
+    if (a.top_k <= 8) return step_form<NB, 8>(a, j, grid, f, s);
+    return step_form<NB, 16>(a, j, grid, f, s);
 }
 
 }  // namespace
@@ -817,8 +1160,8 @@ hipError_t launch_chain_step(const ChainArgs& a, int j, hipStream_t stream) {
     // markov_w2 tile is read once per step for all of them.
     const int nb = a.B > 32 ? 2 : 1;
     dim3 grid(a.nwg, (a.B + 32 * nb - 1) / (32 * nb));
-    const bool pipe = chain_pipelined(a.V);
-    return nb == 2 ? step_kl<2>(a, j, grid, pipe, stream) : step_kl<1>(a, j, grid, pipe, stream);
+    const ChainForm f = chain_form(a.B, a.V, a.r, a.top_k);
+    return nb == 2 ? step_kl<2>(a, j, grid, f, stream) : step_kl<1>(a, j, grid, f, stream);
 }
 
 hipError_t launch_gate(const GateArgs& g, hipStream_t stream) {
