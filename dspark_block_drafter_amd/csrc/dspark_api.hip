@@ -27,11 +27,12 @@ struct Layout {
     size_t winners_off, partials_off, total;
 };
 
-// [flags (256 B)] [winners: n_pred*B u64] [partials: n_pred*B*nwg*top_k u64, top_k > 1]
+// [flags (256 B)] [winners: n_pred*kWinnerWays*winners_stride(B) u64]
+// [partials: n_pred*B*nwg*top_k u64, top_k > 1]
 Layout workspace_layout(int B, int n_pred, int V, int top_k) {
     Layout l;
     l.winners_off = kFlagsBytes;
-    const size_t win = align_up((size_t)n_pred * (size_t)B * 8u);
+    const size_t win = align_up((size_t)n_pred * kWinnerWays * (size_t)winners_stride(B) * 8u);
     l.partials_off = l.winners_off + win;
     const size_t part =
         top_k > 1 ? align_up((size_t)n_pred * B * (size_t)chain_workgroups_max(V) * top_k * 8u) : 0;
@@ -55,6 +56,7 @@ int check_sizes(int B, int L, int H, int V, int layout, int hidden_dtype) {
     const long n_pred = L - first_pred(layout);
     if ((long)B * L > 0x7fffffffL / 2 || (long)B * n_pred * (long)V > (1L << 53))
         return DSPARK_ERR_UNSUPPORTED;
+    if (n_pred * (long)kWinnerWays * winners_stride(B) > 0x7fffffffL) return DSPARK_ERR_UNSUPPORTED;
     if (V >= 0x7fffffff - 1024 || H % 8 != 0) return DSPARK_ERR_UNSUPPORTED;
     return DSPARK_OK;
 }
@@ -110,6 +112,7 @@ int run_chain(const float* logits, const void* hidden, int hidden_dtype, const u
     c.n_pred = n_pred;
     c.top_k = top_k;
     c.nwg = chain_workgroups(B, V, r, top_k);
+    c.wstride = winners_stride(B);
 
     hipError_t e = launch_chain_init(c, stream);
     if (e == hipSuccess && x.p_min_b) {
@@ -153,6 +156,7 @@ int run_chain(const float* logits, const void* hidden, int hidden_dtype, const u
     f.i_first = i_first;
     f.top_k = top_k;
     f.nwg = c.nwg;
+    f.wstride = c.wstride;
     f.hidden_f32 = hidden_dtype == DSPARK_HIDDEN_F32;
     f.p_min = p_min;
     return hip_status(launch_finalize(f, stream));

@@ -61,6 +61,15 @@ inline int chain_workgroups_max(int V) {
     }
     return (V + kChainTileV - 1) / kChainTileV;
 }
+// The running argmax of a (slot, block) is spread over kWinnerWays 64-bit
+// words, which workgroup g raises with atomicMax on word g % kWinnerWays;
+// the argmax is the largest of them. Atomics on one address are serialised
+// (a few hundred per slot on one word cost several microseconds); spread,
+// each word takes a sixteenth of them. Word (j, k, b) sits at
+// (j * kWinnerWays + k) * winners_stride(B) + b, so the words of one block
+// are at least 256 bytes apart.
+constexpr int kWinnerWays = 16;
+inline int winners_stride(int B) { return (B + 31) / 32 * 32; }
 // Flags word bits (the public values of DSPARK_FLAG_*).
 constexpr uint32_t kFlagBadAnchor = 1u, kFlagInternal = 2u, kFlagBadD2t = 4u;
 
@@ -74,11 +83,12 @@ struct ChainArgs {
     const uint16_t* w2;        // [V, r] bf16 bits
     const int64_t* d2t;        // [V] target id of each column, or nullptr (identity)
     const int32_t* anchors;    // [B]
-    unsigned long long* winners;   // [n_pred, B] running argmax keys
+    unsigned long long* winners;   // [n_pred, kWinnerWays, wstride] running argmax keys
     unsigned long long* partials;  // [n_pred, B, nwg, top_k] per-workgroup top-k keys (top_k > 1)
     uint32_t* flags;
     int32_t* lengths;          // [B], set to n_pred here, cut by the confidence head later
     int B, V, r, n_pred, top_k, nwg;
+    int wstride;               // winners_stride(B)
     int vocab;                 // target vocabulary size (== V without d2t)
     const int32_t* stop;       // adaptive gate: slots from *stop on are skipped (nullptr: none)
 };
@@ -86,7 +96,7 @@ hipError_t launch_chain_init(const ChainArgs& a, hipStream_t stream);
 hipError_t launch_chain_step(const ChainArgs& a, int j, hipStream_t stream);
 
 struct FinalArgs {
-    const unsigned long long* winners;
+    const unsigned long long* winners;   // as in ChainArgs
     const unsigned long long* partials;
     const void* hidden;        // [B, L, H] (confidence head only)
     const uint16_t* conf_w;    // [H] or nullptr
@@ -98,6 +108,7 @@ struct FinalArgs {
     int32_t* lengths;          // [B]
     uint32_t* flags;
     int B, L, H, n_pred, i_first, top_k, nwg;
+    int wstride;               // winners_stride(B)
     int V;                     // chain columns (keys outside [0, V) are never mapped)
     int hidden_f32;
     float p_min;

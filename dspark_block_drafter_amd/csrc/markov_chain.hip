@@ -49,6 +49,22 @@ __device__ __forceinline__ long column_token(const int64_t* d2t, int c) {
     return d2t ? (long)d2t[c] : (long)c;
 }
 
+// The running argmax words (kernels.hpp, kWinnerWays): the word workgroup g
+// raises for block b of slot j, and the argmax key of that block and slot.
+__device__ __forceinline__ u64* winner_word(u64* winners, int wstride, int j, int g, int b) {
+    return winners + ((long)j * kWinnerWays + g % kWinnerWays) * wstride + b;
+}
+__device__ __forceinline__ u64 winner_key(const u64* winners, int wstride, int j, int b) {
+    const u64* w = winners + (long)j * kWinnerWays * wstride + b;
+    u64 k[kWinnerWays];
+#pragma unroll
+    for (int i = 0; i < kWinnerWays; ++i) k[i] = w[(long)i * wstride];   // loads issued together
+    u64 m = k[0];
+#pragma unroll
+    for (int i = 1; i < kWinnerWays; ++i) m = k[i] > m ? k[i] : m;
+    return m;
+}
+
 // The previous token of block b for slot j: the anchor, or the target id of
 // the previous slot's argmax column. A value outside [0, vocab) is replaced
 // by 0 and reported (when `report`) in the flags word.
@@ -59,7 +75,7 @@ __device__ __forceinline__ int prev_token(const ChainArgs& a, int j, int b, bool
         t = a.anchors[b];
         bad = kFlagBadAnchor;
     } else {
-        const int c = key_id(a.winners[(long)(j - 1) * a.B + b]);
+        const int c = key_id(winner_key(a.winners, a.wstride, j - 1, b));
         t = (c >= 0 && c < a.V) ? column_token(a.d2t, c) : -1;
         bad = kFlagBadD2t;
     }
@@ -131,7 +147,7 @@ __device__ __forceinline__ void publish(const ChainArgs& a, int j, int bbase, u6
                 for (int i = 0; i < KL; ++i)
                     if (i < a.top_k) p[i] = m[i];
             }
-            if (m[0] != 0ull) atomicMax(a.winners + (long)j * B + b, m[0]);
+            if (m[0] != 0ull) atomicMax(winner_word(a.winners, a.wstride, j, blockIdx.x, b), m[0]);
         }
     }
 }
@@ -502,7 +518,7 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
             for (int i = 0; i < KL; ++i)
                 if (i < a.top_k) p[i] = list[i];
         }
-        if (list[0] != 0ull) atomicMax(a.winners + (long)j * B + b, list[0]);
+        if (list[0] != 0ull) atomicMax(winner_word(a.winners, a.wstride, j, g, b), list[0]);
     }
 }
 
@@ -677,8 +693,9 @@ __global__ __launch_bounds__(256) void chain_step_wave(ChainArgs a, int j) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) z[e] = acc[e];
         const int vlane = vt + 4 * lhalf;
-        if (vt + 32 > V) {
-            // the ragged last tile: plain inserts of the columns inside V
+        if (vt + 32 > V || (KL > 1 && it == 0)) {
+            // plain inserts of the columns inside V (the ragged last tile;
+            // the first step of top-k lists)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int v = vlane + 8 * (e >> 2) + (e & 3);
@@ -702,13 +719,11 @@ __global__ __launch_bounds__(256) void chain_step_wave(ChainArgs a, int j) {
             // columns of the block reach cannot be among its best KL. Bounds:
             // the KL-th best of the union of this lane's list and the partner
             // lane's (both decreasing: the largest over the splits of KL
-            // between them of the smaller of the two closing entries); on the
-            // wave's first tile, when the lists are still short, the smallest
-            // of KL maxima over disjoint groups of the tile's 16 / KL columns,
-            // from either lane of the pair; and the bounds the other waves of
-            // the block group last published. A score equal to the bound
-            // passes, so the full key comparison settles ties by column. Hits
-            // are inserted in rounds, one per lane per round.
+            // between them of the smaller of the two closing entries), and
+            // the bounds the other waves of the block group last published. A
+            // score equal to the bound passes, so the full key comparison
+            // settles ties by column. Hits are inserted in rounds, one per
+            // lane per round.
             float sa[KL], sb[KL];
 #pragma unroll
             for (int i = 0; i < KL; ++i) {
@@ -718,20 +733,6 @@ __global__ __launch_bounds__(256) void chain_step_wave(ChainArgs a, int j) {
             float thr = fmaxf(sa[KL - 1], sb[KL - 1]);
 #pragma unroll
             for (int i = 1; i < KL; ++i) thr = fmaxf(thr, fminf(sa[i - 1], sb[KL - 1 - i]));
-            if (it == 0) {
-                constexpr int GS = 16 / KL;
-                static_assert(GS * KL == 16, "KL divides 16");
-                float tb = INFINITY;
-#pragma unroll
-                for (int gi = 0; gi < KL; ++gi) {
-                    float m = z[gi * GS];
-#pragma unroll
-                    for (int e = 1; e < GS; ++e) m = fmaxf(m, z[gi * GS + e]);
-                    tb = fminf(tb, m);
-                }
-                tb = fmaxf(tb, __shfl_xor(tb, 32, kWave));
-                thr = fmaxf(thr, tb);
-            }
             if (lhalf == 0 && active) s_thr[wave][lrow] = thr;
 #pragma unroll
             for (int w = 0; w < VW; ++w)
@@ -829,7 +830,7 @@ __global__ __launch_bounds__(256) void chain_step_wave(ChainArgs a, int j) {
             for (int i = 0; i < KL; ++i)
                 if (i < a.top_k) p[i] = list[i];
         }
-        if (list[0] != 0ull) atomicMax(a.winners + (long)j * B + bme, list[0]);
+        if (list[0] != 0ull) atomicMax(winner_word(a.winners, a.wstride, j, g, bme), list[0]);
     }
 }
 
@@ -963,7 +964,7 @@ __global__ __launch_bounds__(256) void finalize(FinalArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int B = a.B, n = a.n_pred, k = a.top_k;
     const long o = (long)b * n + j;
-    const u64 win = a.winners[(long)j * B + b];
+    const u64 win = winner_key(a.winners, a.wstride, j, b);
     __shared__ u64 s_list[kWaves][KL];
 
     // Adaptive gate: a slot past its block's cut was not drafted, and a block
@@ -1149,9 +1150,10 @@ hipError_t step_kl(const ChainArgs& a, int j, dim3 grid, ChainForm f, hipStream_
 }  // namespace
 
 hipError_t launch_chain_init(const ChainArgs& a, hipStream_t stream) {
-    const int n = a.n_pred * a.B > a.B ? a.n_pred * a.B : a.B;
-    hipLaunchKernelGGL(chain_init, dim3((n + 255) / 256), dim3(256), 0, stream, a.winners,
-                       a.n_pred * a.B, a.flags, a.lengths, a.B, a.n_pred);
+    const int nw = a.n_pred * kWinnerWays * a.wstride;   // < 2^31 (checked on the host)
+    const int n = nw > a.B ? nw : a.B;
+    hipLaunchKernelGGL(chain_init, dim3((n + 255) / 256), dim3(256), 0, stream, a.winners, nw,
+                       a.flags, a.lengths, a.B, a.n_pred);
     return hipGetLastError();
 }
 
