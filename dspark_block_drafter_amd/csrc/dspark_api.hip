@@ -74,6 +74,11 @@ int check_chain_args(int V, int r, int top_k, float p_min, const void* w1, const
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP; }
 
+// A call judges its launches by hipGetLastError, so an error left pending by
+// an earlier HIP call of the caller (or of another library in the process)
+// is cleared first rather than reported as the library's own.
+void clear_pending_error() { (void)hipGetLastError(); }
+
 // Options of the chain beyond the plain step.
 struct ChainExtras {
     const int64_t* d2t = nullptr;     // reduced draft vocabulary: column c is target id d2t[c]
@@ -114,6 +119,7 @@ int run_chain(const float* logits, const void* hidden, int hidden_dtype, const u
     c.nwg = chain_workgroups(B, V, r, top_k);
     c.wstride = winners_stride(B);
 
+    clear_pending_error();
     hipError_t e = launch_chain_init(c, stream);
     if (e == hipSuccess && x.p_min_b) {
         GateArgs g;
@@ -193,6 +199,7 @@ int dspark_logits(const void* hidden, int hidden_dtype, const uint16_t* lm_head,
     g.K = H;
     g.L = L;
     g.i_first = i_first;
+    clear_pending_error();
     return hip_status(launch_lmhead_gemm(g, hidden_dtype == DSPARK_HIDDEN_F32,
                                          static_cast<hipStream_t>(stream)));
 }
@@ -329,6 +336,7 @@ int dspark_verify(const int32_t* candidates, const int32_t* lengths, const int32
     v.n_pred = n_pred;
     v.top_k = top_k;
     v.width = lattice ? top_k : 1;
+    clear_pending_error();
     return hip_status(launch_verify(v, static_cast<hipStream_t>(stream)));
 }
 

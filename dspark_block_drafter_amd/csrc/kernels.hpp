@@ -64,11 +64,12 @@ inline int chain_workgroups_max(int V) {
 // The running argmax of a (slot, block) is spread over kWinnerWays 64-bit
 // words, which workgroup g raises with atomicMax on word g % kWinnerWays;
 // the argmax is the largest of them. Atomics on one address are serialised
-// (a few hundred per slot on one word cost several microseconds); spread,
-// each word takes a sixteenth of them. Word (j, k, b) sits at
-// (j * kWinnerWays + k) * winners_stride(B) + b, so the words of one block
-// are at least 256 bytes apart.
-constexpr int kWinnerWays = 16;
+// (256-512 per slot on one word cost 2-5 us per slot); spread, each word
+// takes an eighth of them, and a reader loads eight words. (4 and 8 ways
+// time the same; 16 and 32 lose more on the reads than they gain.) Word
+// (j, k, b) sits at (j * kWinnerWays + k) * winners_stride(B) + b, so the
+// words of one block are at least 256 bytes apart.
+constexpr int kWinnerWays = 8;
 inline int winners_stride(int B) { return (B + 31) / 32 * 32; }
 // Flags word bits (the public values of DSPARK_FLAG_*).
 constexpr uint32_t kFlagBadAnchor = 1u, kFlagInternal = 2u, kFlagBadD2t = 4u;

@@ -78,6 +78,9 @@ typedef enum {
     DSPARK_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than dspark_workspace_bytes */
     DSPARK_ERR_HIP = -4          /* the HIP runtime reported an error while enqueuing     */
 } dspark_status;
+/* An error left pending in the HIP runtime by an earlier call outside the
+ * library is cleared when an entry point starts enqueuing; only errors of the
+ * library's own launches are reported as DSPARK_ERR_HIP. */
 
 typedef enum {
     DSPARK_LAYOUT_ANCHOR_FIRST = 0,
