@@ -564,7 +564,19 @@ hipError_t launch_lmhead_gemm(const GemmArgs& a, bool hidden_f32, hipStream_t st
         // Stage rows of 64 K values (one 128-byte line each) where K allows:
         // 6-15% faster than 32-value rows at M = 16, 24 and 128 (same sums).
         if (a.K % 64 == 0) {
-            if (a.M > 32) return launch_dma<128, 128, 2, 2, 4, 64>(a, stream);
+            // 32 < M <= 128: 256 lm_head rows per tile (the hidden rows, read
+            // again by every tile from L2, are half the copies of a step
+            // instead of the same number), eight waves; 10% faster than 128
+            // rows at M = 128.
+            if (a.M > 32) return launch_dma<128, 256, 2, 4, 3, 64>(a, stream);
+            // M <= 32: 128 lm_head rows per tile and two workgroups per CU,
+            // unless the last round of 2 x 256 workgroups would run less than
+            // half full: then 64 rows and three per CU, whose tail is shorter
+            // (Qwen3-8B: 1187 tiles, 292 -> 245 us; at 2048 tiles, Gemma-4,
+            // 128 rows stay faster, 252 against 278 us).
+            constexpr long kSlots = 2 * 256;
+            const long rem = (a.N + 127) / 128 % kSlots;
+            if (rem != 0 && rem < kSlots / 2) return launch_dma<32, 64, 1, 2, 4, 64>(a, stream);
             return launch_dma<32, 128, 1, 2, 4, 64>(a, stream);
         }
         if (a.M > 32) return launch_dma<128, 128, 2, 2, 6>(a, stream);
