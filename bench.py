@@ -36,8 +36,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # reported for any other source or workload.
 GEMM_TRAFFIC = {
     "workload": "qwen38_27b_throughput",
-    "source_sha256": "c6047edb2e7bead590f9655377786901b29c52f02ea42c52d92ab8159fcbc7cf",
-    "bytes": 5633881750,
+    "source_sha256": "e3a5bed756b7dc0d5818a403ee7bf5ff802de82f2062b7cbde864a58d859fc8a",
+    "bytes": 5702762617,
 }
 
 
