@@ -44,12 +44,38 @@ inline ChainForm chain_form(int B, int V, int r, int top_k) {
     if ((r + 15) / 16 > 8) return kChainPipeDeep;
     return (B > 32 && top_k > 1) ? kChainPipeTwo : kChainWave;
 }
+// Per-wave form: the logits rows a wave stages per step (only the blocks of
+// its group that exist: 8, 16 or 32; top-k lists longer than 4 always take
+// 32), and whether it runs two workgroups per CU: with 8 or 16 rows, when two
+// workgroups of four waves with at least two stages each fit the CU's 160 KB
+// (a stage is 32 markov_w2 rows of the rank, rounded up to 32, 64 or 128,
+// plus the logits rows of 128 bytes). A second workgroup hides one's inserts
+// and waits behind the other's: chain + finalize 330 -> 315 us on the B = 8
+// top-4 tree, 57 -> 54 us at the Gemma shape, Qwen3-8B unchanged; staging
+// fewer rows with one workgroup per CU and a deeper ring alone was slower
+// (353 / 66 / 122 us).
+inline int chain_wave_rows(int B, int top_k) {
+    if (top_k > 4 || B > 16) return 32;
+    return B <= 8 ? 8 : 16;
+}
+inline int chain_wave_rank(int r) {
+    const int rs = (r + 15) / 16;
+    return rs == 0 ? 0 : rs <= 2 ? 2 : rs <= 4 ? 4 : 8;
+}
+constexpr int chain_wave_stage_bytes(int RS, int LROWS) { return (64 * RS + 8 * LROWS) * 16; }
+constexpr int kChainWaveBudget2 = 79 * 1024;    // per workgroup, two per CU
+constexpr int kChainWaveBudget1 = 158 * 1024;   // one per CU
+inline int chain_wave_per_cu(int B, int r, int top_k) {
+    const int rows = chain_wave_rows(B, top_k);
+    return rows < 32 && 4 * 2 * chain_wave_stage_bytes(chain_wave_rank(r), rows) <= kChainWaveBudget2 ? 2 : 1;
+}
 inline int chain_workgroups(int B, int V, int r, int top_k) {
     const ChainForm f = chain_form(B, V, r, top_k);
     if (f == kChainDirect) return (V + kChainTileV - 1) / kChainTileV;
     const int ts = chain_tile(B, r);
     const int nt = (V + ts - 1) / ts;
-    const int cap = f == kChainPipeTwo ? kChainMaxWGs : kChainCUs;
+    const int cap = f == kChainPipeTwo ? kChainMaxWGs
+                    : f == kChainWave ? kChainCUs * chain_wave_per_cu(B, r, top_k) : kChainCUs;
     return nt < cap ? nt : cap;
 }
 // Upper bound of chain_workgroups over every rank (workspace sizing does not

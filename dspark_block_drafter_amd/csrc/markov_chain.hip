@@ -536,7 +536,7 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
 // The waves that score the same blocks share their top-k bounds through LDS
 // without synchronisation: every published value is a valid bound whenever
 // it is read. The workgroup merges and publishes once per slot.
-template <int NB, int KL, int RS, int NS>
+template <int NB, int KL, int RS, int NS, int LROWS>
 __global__ __launch_bounds__(256) void chain_step_wave(ChainArgs a, int j) {
     constexpr int VW = kWaves / NB;         // 32-column blocks per tile
     constexpr int TS = 32 * VW;             // columns per tile
@@ -544,14 +544,15 @@ __global__ __launch_bounds__(256) void chain_step_wave(ChainArgs a, int j) {
     constexpr int WRd = WR > 0 ? WR : 1;
     constexpr int LR = 8;                   // 16-byte chunks per staged logits row (32 columns)
     constexpr int W_SLOTS = 32 * WR;
-    constexpr int L_SLOTS = 32 * LR;
+    constexpr int L_SLOTS = LROWS * LR;     // the logits rows of the group's blocks that exist
     constexpr int STAGE = W_SLOTS + L_SLOTS;
     constexpr int W_INST = W_SLOTS / 64, L_INST = L_SLOTS / 64;
     constexpr int LW = W_INST + L_INST;     // copies per tile per wave
     static_assert(NB == 1 || NB == 2, "one or two block groups");
     static_assert(NS >= 2 && NS * LW + RS < 64, "vmcnt range");
+    static_assert(LROWS == 8 || LROWS == 16 || LROWS == 32, "staged logits rows");
     static_assert(RS * 64 <= STAGE, "W1 rows fit one stage");
-    static_assert(KL * 32 * 8 <= STAGE * 16, "list merge reuses a wave's ring");
+    static_assert(KL * 32 * 8 <= NS * STAGE * 16, "list merge reuses a wave's ring");
     __shared__ u32x4 ring[kWaves][NS][STAGE];
     // Top-k bound of each wave's lane pairs, per block (see consume below).
     __shared__ float s_thr[kWaves][32];
@@ -675,7 +676,10 @@ __global__ __launch_bounds__(256) void chain_step_wave(ChainArgs a, int j) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int c = 2 * q + lhalf;
-            const f32x4 x = __builtin_bit_cast(f32x4, stg[W_SLOTS + lrow * LR + (c ^ swz_rows<LR>(lrow))]);
+            // rows past LROWS hold no block: their lanes score zeros
+            const int lr = lrow < LROWS ? lrow : 0;
+            f32x4 x = __builtin_bit_cast(f32x4, stg[W_SLOTS + lr * LR + (c ^ swz_rows<LR>(lr))]);
+            if (LROWS < 32 && lrow >= LROWS) x = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[4 * q + e] = x[e];
         }
@@ -1111,19 +1115,46 @@ hipError_t step_pipe(const ChainArgs& a, int j, dim3 grid, bool two, hipStream_t
     return hipGetLastError();
 }
 
-// Per-wave rings: as many stages as fit 4 x NS x stage <= 159 KB (stage =
-// 32 markov_w2 rows of the rank plus 32 logits rows of 32 columns).
-template <int NB, int KL>
-hipError_t step_wave(const ChainArgs& a, int j, dim3 grid, hipStream_t s) {
-    const int rs = (a.r + 15) / 16;
-#define DSPARK_STEP(RSV, NSV) hipLaunchKernelGGL((chain_step_wave<NB, KL, RSV, NSV>), grid, dim3(256), 0, s, a, j);
-    if (rs == 0) { DSPARK_STEP(0, 8) }
-    else if (rs <= 2) { DSPARK_STEP(2, 6) }
-    else if (rs <= 4) { DSPARK_STEP(4, 4) }
-    else if (rs <= 8) { DSPARK_STEP(8, 3) }
+// Per-wave rings: as many stages as fit the workgroup's share of the CU's
+// LDS (chain_wave_per_cu), at most 8.
+template <int RS, int LROWS, int WPC>
+constexpr int chain_wave_stages() {
+    const int n = (WPC == 2 ? kChainWaveBudget2 : kChainWaveBudget1) / (4 * chain_wave_stage_bytes(RS, LROWS));
+    return n > 8 ? 8 : n;
+}
+
+template <int NB, int KL, int LROWS>
+hipError_t step_wave_rows(const ChainArgs& a, int j, dim3 grid, hipStream_t s) {
+    const int rs = chain_wave_rank(a.r);
+    const bool two = chain_wave_per_cu(a.B, a.r, a.top_k) == 2;
+#define DSPARK_STEP(RSV, WPCV)                                                                 \
+    hipLaunchKernelGGL((chain_step_wave<NB, KL, RSV, chain_wave_stages<RSV, LROWS, WPCV>(), LROWS>), \
+                       grid, dim3(256), 0, s, a, j);
+#define DSPARK_RANK(RSV)                                                                     \
+    if constexpr (LROWS < 32 && chain_wave_stages<RSV, LROWS, 2>() >= 2) {                   \
+        if (two) { DSPARK_STEP(RSV, 2) }                                                     \
+        else { DSPARK_STEP(RSV, 1) }                                                         \
+    } else {                                                                                 \
+        DSPARK_STEP(RSV, 1)                                                                  \
+    }
+    if (rs == 0) { DSPARK_RANK(0) }
+    else if (rs == 2) { DSPARK_RANK(2) }
+    else if (rs == 4) { DSPARK_RANK(4) }
+    else if (rs == 8) { DSPARK_RANK(8) }
     else return hipErrorInvalidValue;   // chain_form never picks this form for a wider rank
+#undef DSPARK_RANK
 #undef DSPARK_STEP
     return hipGetLastError();
+}
+
+template <int NB, int KL>
+hipError_t step_wave(const ChainArgs& a, int j, dim3 grid, hipStream_t s) {
+    if constexpr (NB == 1 && KL <= 4) {
+        const int lr = chain_wave_rows(a.B, a.top_k);
+        if (lr == 8) return step_wave_rows<NB, KL, 8>(a, j, grid, s);
+        if (lr == 16) return step_wave_rows<NB, KL, 16>(a, j, grid, s);
+    }
+    return step_wave_rows<NB, KL, 32>(a, j, grid, s);
 }
 
 template <int NB, int KL>

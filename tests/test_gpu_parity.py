@@ -78,6 +78,11 @@ SMALL = {
     "long_lists_one_group": lambda: make_small(8, 3, 64, 229412, 128, top_k=4, conf=True,
                                                p_min=0.3, seed=27),
     "long_lists_r64": lambda: make_small(40, 3, 64, 110000, 64, top_k=4, seed=28),
+    # per-wave rings staging 16 logits rows: two workgroups per CU (rank 64,
+    # top-4, several steps per wave) and one per CU (rank 128, top-1)
+    "rows16_two_per_cu": lambda: make_small(12, 3, 64, 229412, 64, top_k=4, conf=True, p_min=0.3,
+                                            seed=29),
+    "rows16_rank128_top1": lambda: make_small(16, 3, 64, 160000, 128, top_k=1, seed=30),
     "reduced_vocab": lambda: make_small(4, 7, 176, 4096, 64, top_k=4, layout=BONUS_ANCHOR,
                                         reachable=300, conf=True, p_min=0.5, conf_trend=True,
                                         seed=10),
