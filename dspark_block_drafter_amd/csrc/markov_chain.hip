@@ -9,19 +9,21 @@
 // (lucebox PR #626 "feat(qwen38): add adaptive concurrent DSpark
 // speculation", description).
 //
-// One launch per slot j. A workgroup owns kChainTileV vocabulary columns for
-// up to 64 blocks. Before it needs them it stages, with coalesced
-// direct-to-LDS loads, the markov_w2 rows of its columns and the slot-j
-// logits of its blocks; meanwhile it gathers the rank-r rows
-// markov_w1[prev_b] (the MFMA B operand, kept in registers). The [v x b]
-// bias tile is one bf16 MFMA product per 32 columns; the logits are added and
-// every lane keeps a running top-k for its block. The 32x32 accumulator
-// layout gives every lane a single block b and 16 vocabulary ids, so the
-// per-lane lists see their ids in increasing order. Lists are merged across
-// the two lanes that share b, then across the four waves through LDS; the
-// workgroup's best key goes to a 64-bit atomicMax on the slot's running
-// argmax word (keys order by score, then lower id), and its list to the
-// partials used to assemble the candidates after the last slot.
+// One launch per slot j. A workgroup owns a contiguous range of vocabulary
+// columns for up to 64 blocks. It stages, with coalesced direct-to-LDS loads,
+// the markov_w2 rows of its columns and the slot-j logits of its blocks,
+// through a ring shared by its four waves (chain_step_pipe) or one private
+// ring per wave (chain_step_wave); the rank-r rows markov_w1[prev_b] become
+// the MFMA B operand. The [v x b] bias tile is one bf16 MFMA product per 32
+// columns with the logits as accumulator input, and every lane keeps a
+// running top-k for its block. The 32x32 accumulator layout gives every lane
+// a single block b and 16 vocabulary ids, so the per-lane lists see their ids
+// in increasing order. Lists are merged across the two lanes that share b,
+// then across the waves through LDS; the workgroup's best key goes to a
+// 64-bit atomicMax on one of the slot's running-argmax words for b (keys
+// order by score, then lower id), and its list to the partials used to
+// assemble the candidates after the last slot. chain_step_direct reads its
+// operands straight from global memory for any V.
 #include "common.hpp"
 #include "kernels.hpp"
 
