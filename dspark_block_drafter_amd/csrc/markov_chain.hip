@@ -526,18 +526,19 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
 
 // ---- step kernel for V % 4 == 0: a private ring per wave ----------------------
 
-// Wave w of workgroup g scores the 32-column block w % VW of every tile in
-// the workgroup's range [t0, t1) (TS = 32 VW columns per tile) for the block
-// group w / VW (VW = 2 for two groups of 32 blocks, 4 for one group). Each
-// wave streams its own markov_w2 rows and slot-j logits rows through its own
+// The workgroup's range of tiles [t0, t1) (TS = 32 VW columns per tile) is
+// cut into VW contiguous runs of 32-column steps; wave w scores run w % VW
+// for the block group w / VW (VW = 2 for two groups of 32 blocks, 4 for one
+// group). Each wave streams its own markov_w2 rows and slot-j logits rows
+// (LROWS of them: only the group's blocks that exist) through its own
 // NS-stage LDS ring of direct-to-LDS copies, so its loop needs no workgroup
 // barrier: a slow insert round holds up only that wave, and all NS stages are
-// in flight while it inserts (a stage is refilled as soon as its tile has
+// in flight while it inserts (a stage is refilled as soon as its step has
 // been read into the accumulators). With two block groups the two waves of a
-// column block both copy its markov_w2 rows (the second copy is an L2 hit).
-// The waves that score the same blocks share their top-k bounds through LDS
-// without synchronisation: every published value is a valid bound whenever
-// it is read. The workgroup merges and publishes once per slot.
+// run both copy its markov_w2 rows (the second copy is an L2 hit). The waves
+// that score the same blocks share their top-k bounds through LDS without
+// synchronisation: every published value is a valid bound whenever it is
+// read. The workgroup merges and publishes once per slot.
 template <int NB, int KL, int RS, int NS, int LROWS>
 __global__ __launch_bounds__(256) void chain_step_wave(ChainArgs a, int j) {
     constexpr int VW = kWaves / NB;         // 32-column blocks per tile
