@@ -569,10 +569,14 @@ hipError_t launch_lmhead_gemm(const GemmArgs& a, bool hidden_f32, hipStream_t st
         // 6-15% faster than 32-value rows at M = 16, 24 and 128 (same sums).
         if (a.K % 64 == 0) {
             // 32 < M <= 128: 256 lm_head rows per tile (the hidden rows, read
-            // again by every tile from L2, are half the copies of a step
-            // instead of the same number), eight waves; 10% faster than 128
-            // rows at M = 128.
-            if (a.M > 32) return launch_dma<128, 256, 2, 4, 3, 64>(a, stream);
+            // again by every tile from L2, are a third of a step's copies
+            // instead of half), eight waves; 10% faster than 128 rows at
+            // M = 128. A vocabulary too small to give every CU a tile that
+            // way keeps 128 rows.
+            if (a.M > 32) {
+                if ((a.N + 255) / 256 >= 256) return launch_dma<128, 256, 2, 4, 3, 64>(a, stream);
+                return launch_dma<128, 128, 2, 2, 4, 64>(a, stream);
+            }
             // M <= 32: 128 lm_head rows per tile and two workgroups per CU,
             // unless the last round of 2 x 256 workgroups would run less than
             // half full: then 64 rows and three per CU, whose tail is shorter

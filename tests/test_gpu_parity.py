@@ -56,6 +56,9 @@ SMALL = {
     "mid_gemm_M33": lambda: make_small(11, 3, 1032, 4097, 32, top_k=2, seed=8),
     "rank256": lambda: make_small(6, 4, 128, 1536, 256, top_k=3, seed=9, w_std=0.2),
     "dma_mid_M63": lambda: make_small(9, 7, 160, 3001, 16, top_k=2, conf=True, p_min=0.4, seed=18),
+    # 32 < M <= 128 with H % 64 == 0 and too few 256-row tiles for the CUs:
+    # the 128-row tiles with 64-value stage rows, ragged M and N
+    "dma_mid_small_vocab": lambda: make_small(10, 6, 128, 5000, 16, top_k=2, seed=32),
     "dma_big_K32": lambda: make_small(20, 13, 32, 700, 8, top_k=3, seed=19),
     "dma_big_K96_bonus": lambda: make_small(23, 12, 96, 1000, 24, top_k=1, layout=BONUS_ANCHOR,
                                              conf=True, p_min=0.5, seed=20),
