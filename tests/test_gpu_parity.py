@@ -86,6 +86,12 @@ SMALL = {
     "rows16_two_per_cu": lambda: make_small(12, 3, 64, 229412, 64, top_k=4, conf=True, p_min=0.3,
                                             seed=29),
     "rows16_rank128_top1": lambda: make_small(16, 3, 64, 160000, 128, top_k=1, seed=30),
+    "rows16_rank128_top4": lambda: make_small(12, 3, 64, 160000, 128, top_k=4, seed=33),
+    # 8 staged rows, two workgroups per CU: rank 0 (eight-stage rings) and
+    # rank 24 (six stages), several steps per wave
+    "rows8_rank0_top4": lambda: make_small(4, 4, 64, 300000, 0, top_k=4, seed=34),
+    "rows8_rank24_top3": lambda: make_small(3, 4, 64, 300000, 24, top_k=3, conf=True, p_min=0.4,
+                                            seed=35),
     "reduced_vocab": lambda: make_small(4, 7, 176, 4096, 64, top_k=4, layout=BONUS_ANCHOR,
                                         reachable=300, conf=True, p_min=0.5, conf_trend=True,
                                         seed=10),
