@@ -36,8 +36,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # reported for any other source or workload.
 GEMM_TRAFFIC = {
     "workload": "qwen38_27b_throughput",
-    "source_sha256": "e3a5bed756b7dc0d5818a403ee7bf5ff802de82f2062b7cbde864a58d859fc8a",
-    "bytes": 5702762617,
+    "source_sha256": "9a6f3f13ff5256ed76b086a2566776f659b28fa6246ceb8e1eaf73f0ce808bfc",
+    "bytes": 5607210342,
 }
 
 
