@@ -92,6 +92,12 @@ SMALL = {
     "rows8_rank0_top4": lambda: make_small(4, 4, 64, 300000, 0, top_k=4, seed=34),
     "rows8_rank24_top3": lambda: make_small(3, 4, 64, 300000, 24, top_k=3, conf=True, p_min=0.4,
                                             seed=35),
+    # more than 64 blocks over a long vocabulary: two block groups of 64 in the
+    # grid, each with the full workgroup count (per-wave form at top-1, the
+    # two-stage ring at top-4)
+    "B96_two_groups_wave_top1": lambda: make_small(96, 3, 64, 100000, 64, top_k=1, seed=36),
+    "B80_two_groups_pipe_top4": lambda: make_small(80, 3, 64, 100000, 128, top_k=4, conf=True,
+                                                   p_min=0.3, seed=37),
     "reduced_vocab": lambda: make_small(4, 7, 176, 4096, 64, top_k=4, layout=BONUS_ANCHOR,
                                         reachable=300, conf=True, p_min=0.5, conf_trend=True,
                                         seed=10),
