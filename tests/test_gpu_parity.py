@@ -66,6 +66,9 @@ SMALL = {
     # several K steps; two K steps (loads past the end are clamped)
     "w4_ragged_K320": lambda: make_small(37, 8, 320, 3000, 16, top_k=2, conf=True, p_min=0.4, seed=21),
     "w4_two_ksteps": lambda: make_small(33, 9, 128, 1000, 8, top_k=1, layout=BONUS_ANCHOR, seed=22),
+    # a tile count that is not a multiple of 8 (plain tile order, no XCD
+    # grouping) and an odd number of K steps
+    "w4_six_tiles_K192": lambda: make_small(40, 9, 192, 700, 8, top_k=2, seed=38),
     # several tiles per workgroup (V > 256 tiles): the two-stage ring of
     # top-k over two block groups (2-3 tiles each of 512 workgroups), the
     # four-stage ring with fewer tiles than stages (2-3 of 256) and with more
