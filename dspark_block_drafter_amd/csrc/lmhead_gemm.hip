@@ -328,6 +328,9 @@ __global__ __launch_bounds__(64 * WM * WN) void lmhead_gemm_dma(GemmArgs a) {
     for (int kt = 0; kt < nK; ++kt) {
         // Tile kt must have landed: at most min(NS-2, nK-1-kt) newer tiles may still fly.
         wait_stages<LW, NS - 2>(min(NS - 2, nK - 1 - kt));
+        // this wave's reads of stage kt-1 (previous iteration) have returned
+        // before the barrier lets any wave refill that stage
+        wait_lds_reads();
         block_barrier();  // every wave's part of tile kt is in LDS; stage kt-1 is free
         const int kn = kt + NS - 1;
         if (kn < nK) issue(kn % NS, kn * BKS);

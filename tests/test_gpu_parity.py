@@ -3,9 +3,8 @@
 Small cases run the oracle on every block; they span several GEMM and chain
 tiles, ragged M / N / K tails, both block layouts, fp32 and bf16 hidden
 states, ranks from 0 to 256, top_k from 1 to 16 and more than 64 blocks. The
-full-size workloads are checked on sampled blocks (every block's chain is
-independent, so a sampled block is checked completely: all its logits, every
-slot's token and candidates, its confidences and its cut).
+full-size workloads are checked against the oracle on every block: all its
+logits, every slot's token and candidates, its confidences and its cut.
 """
 from __future__ import annotations
 
@@ -101,6 +100,14 @@ SMALL = {
     "B96_two_groups_wave_top1": lambda: make_small(96, 3, 64, 100000, 64, top_k=1, seed=36),
     "B80_two_groups_pipe_top4": lambda: make_small(80, 3, 64, 100000, 128, top_k=4, conf=True,
                                                    p_min=0.3, seed=37),
+    # fp32 hidden states with more than 32 rows: the register-staged GEMM with
+    # 128-row tiles, K a multiple of 64 (whole K steps) and not (H = 200:
+    # the last K step is partly past H)
+    "f32_M45_K192": lambda: make_small(9, 5, 192, 3001, 16, top_k=2, hidden_f32=True, conf=True,
+                                       p_min=0.4, seed=39),
+    "f32_M45_K200": lambda: make_small(9, 5, 200, 2900, 16, top_k=3, hidden_f32=True, seed=40),
+    "f32_M300_K200_bonus": lambda: make_small(50, 7, 200, 1500, 8, top_k=1, layout=BONUS_ANCHOR,
+                                              hidden_f32=True, seed=47),
     "reduced_vocab": lambda: make_small(4, 7, 176, 4096, 64, top_k=4, layout=BONUS_ANCHOR,
                                         reachable=300, conf=True, p_min=0.5, conf_trend=True,
                                         seed=10),
@@ -409,24 +416,25 @@ def test_verify_own_chain_accepts_whole_blocks(dev):
     assert tot.cpu().numpy().tolist() == [int(res["lengths"].sum())] * 2
 
 
-# ---- full-size workloads, sampled blocks ------------------------------------
+# ---- full-size workloads, every block ------------------------------------------
 
-FULL = {
-    "qwen3_8b": [0],
-    "gemma4_26b_a4b": [0, 1, 2, 3],
-    "qwen38_27b_tree": [0, 7],
-    "qwen38_27b_throughput": [0, 63],
-}
+FULL = ["qwen3_8b", "gemma4_26b_a4b", "qwen38_27b_tree", "qwen38_27b_throughput"]
 
 
-@pytest.mark.parametrize("name", list(FULL))
-def test_full_size_sampled(dev, orc, name):
+@pytest.mark.parametrize("name", FULL)
+def test_full_size(dev, orc, name):
+    import time
     inp = make_inputs(CONFIGS[name])
     _say(f"[full] {name}: generated inputs")
     g = _gpu(inp)
-    _say(f"[full] {name}: GPU done, checking blocks {FULL[name]}")
-    reps = check(orc, inp, g, blocks=FULL[name])
-    _say(f"[full] {name}: ok {reps}")
+    _say(f"[full] {name}: GPU done, checking all {inp.cfg.B} blocks against the oracle")
+    reps = []
+    t0 = time.perf_counter()
+    for b in range(inp.cfg.B):
+        reps += check(orc, inp, g, blocks=[b])
+        _say(f"[full] {name}: block {b} ok ({time.perf_counter() - t0:.0f} s)")
+    _say(f"[full] {name}: max logit err {max(r['max_logit_err'] for r in reps):.3g}, "
+         f"near ties {sum(r['near_tie'] for r in reps)}")
     c = inp.cfg
     # properties that hold for every block, checked on all of them
     assert g["tokens"].shape == (c.B, c.n_pred)
