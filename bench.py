@@ -8,9 +8,12 @@ Qwen3.8-27B shape (B=64 blocks of L=16 anchor-first slots, H=5120,
 V=248320, r=128, top_k=4, p_min=0.3); inputs are resident in HBM before the
 timed region starts. Prints one JSON line.
 
-Per-kernel figures come from a second timed loop that issues the same two
-halves separately (dspark_logits, then dspark_chain) with HIP events on the
-launch stream between them.
+Per-kernel figures come from the timed steps themselves: each step is a
+dspark_propose_marked call, which records HIP events on the launch stream
+between its launches (after the set-up kernel, after the lm_head projection,
+after the last chain step), and the bench records one event before and one
+after every call. An unmarked loop of dspark_propose calls is timed beside it
+as a cross-check that the events cost nothing.
 """
 from __future__ import annotations
 
@@ -74,18 +77,46 @@ def calibrate_copy(mib: int, reps: int) -> int:
     return 0
 
 
-def cpu_baseline(inp, blocks: int) -> dict:
-    """The oracle as it stands, on the host cores, over the first `blocks` blocks."""
+def host_cpu() -> str:
+    """The host's CPU model (lscpu), for the record of the CPU baseline."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+    except (OSError, subprocess.SubprocessError):
+        return "unknown"
+    for line in out.splitlines():
+        if line.startswith("Model name:"):
+            return line.split(":", 1)[1].strip()
+    return "unknown"
+
+
+def cpu_baseline(inp, blocks: int, single_blocks: int) -> dict:
+    """The oracle as it stands (OpenMP over the vocabulary), on the host
+    cores: `blocks` blocks on every OpenMP thread, then `single_blocks` on one."""
+    import ctypes
     from oracle import Oracle
     orc = Oracle()
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    t0 = time.perf_counter()
-    orc.propose(inp, blocks=list(range(blocks)), keep_logits=False)
-    dt = time.perf_counter() - t0
+    gomp = ctypes.CDLL("libgomp.so.1")   # the OpenMP runtime the oracle is linked with
+    cores = int(gomp.omp_get_max_threads())
+
+    def run(nb: int):
+        t0 = time.perf_counter()
+        orc.propose(inp, blocks=list(range(nb)), keep_logits=False)
+        return time.perf_counter() - t0
+
+    dt = run(blocks)
     toks = blocks * inp.cfg.n_pred
+    gomp.omp_set_num_threads(1)
+    dt1 = run(single_blocks)
+    gomp.omp_set_num_threads(cores)
+    toks1 = single_blocks * inp.cfg.n_pred
     return {"value": toks / dt, "unit": "drafted tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{blocks} of {inp.cfg.B} blocks ({toks} drafted tokens) of the same "
-                      f"workload, {dt:.1f} s wall on {cores} OpenMP threads"}
+                      f"workload, {dt:.1f} s wall on {cores} OpenMP threads",
+            "single_thread": {"value": toks1 / dt1, "cores": 1,
+                              "sample": f"{single_blocks} block ({toks1} drafted tokens), "
+                                        f"{dt1:.1f} s wall on 1 thread"},
+            "host": {"cpu": host_cpu(), "nproc": os.cpu_count()}}
 
 
 def main() -> int:
@@ -95,6 +126,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen38_27b_throughput")
     ap.add_argument("--cpu-blocks", type=int, default=2)
+    ap.add_argument("--cpu-single-blocks", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--adaptive", action="store_true",
                     help="run dspark_propose_adaptive (confidence gate before the chain, "
@@ -169,7 +201,15 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} done")
 
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    def event():
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record(stream)   # creates the HIP event before the timed region
+        return ev
+
+    plain = not (args.d2t or args.adaptive)
+    # Unmarked steps: the cross-check (and the timed region of the d2t and
+    # adaptive forms, which have no marked entry point).
+    ev0, ev1 = event(), event()
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     ev0.record(stream)
@@ -178,33 +218,54 @@ def main() -> int:
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    ms = ev0.elapsed_time(ev1) / args.steps
-    log(f"timed {args.steps} steps: {ms:.3f} ms/step (events), {1e3 * wall / args.steps:.3f} ms/step (wall)")
+    ms_unmarked = ev0.elapsed_time(ev1) / args.steps
+    log(f"{args.steps} unmarked steps: {ms_unmarked:.3f} ms/step (events), "
+        f"{1e3 * wall / args.steps:.3f} ms/step (wall)")
+
+    phases = None
+    if plain:
+        # The timed region: marked steps. Events per step: before the call,
+        # after the set-up kernel, after the projection, after the last chain
+        # step, after the call.
+        evs = [[event() for _ in range(5)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        for e in evs:
+            e[0].record(stream)
+            dsp.propose(d["hidden"], d["lm_head"], d["markov_w1"], d["markov_w2"], d["anchors"],
+                        layout=cfg.layout, top_k=cfg.top_k, p_min=cfg.p_min,
+                        lm_head_bias=d["lm_head_bias"], conf_w=d["conf_w"], out=out,
+                        stream=stream, marks=(e[1], e[2], e[3]))
+            e[4].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        ms = evs[0][0].elapsed_time(evs[-1][4]) / args.steps
+        avg = lambda a, b: sum(e[a].elapsed_time(e[b]) for e in evs) / args.steps
+        phases = {"init": avg(0, 1), "gemm": avg(1, 2), "chain": avg(2, 3), "finalize": avg(3, 4)}
+        gemm_ms, chain_ms = phases["gemm"], phases["chain"] + phases["finalize"]
+        log(f"timed {args.steps} marked steps: {ms:.3f} ms/step (events), "
+            f"{1e3 * wall / args.steps:.3f} ms/step (wall); set-up {phases['init'] * 1e3:.1f} us, "
+            f"lm_head GEMM {gemm_ms * 1e3:.1f} us, chain steps {phases['chain'] * 1e3:.1f} us, "
+            f"finalize {phases['finalize'] * 1e3:.1f} us")
+    else:
+        ms = ms_unmarked
+        # the projection alone through dspark_logits (the chain's time is the
+        # step minus it)
+        evs = [[event() for _ in range(2)] for _ in range(args.steps)]
+        for e in evs:
+            e[0].record(stream)
+            dsp.logits(d["hidden"], d["lm_head"], layout=cfg.layout,
+                       lm_head_bias=None if args.d2t else d["lm_head_bias"], out=out.logits,
+                       stream=stream)
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        gemm_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+        chain_ms = ms - gemm_ms
+        log(f"lm_head GEMM alone {gemm_ms * 1e3:.1f} us, rest of the step {chain_ms * 1e3:.1f} us")
     assert dsp.read_flags(out) == 0
     submitted = int(out.lengths.sum().item())
     if args.adaptive:
         log(f"adaptive gate: {submitted} of {cfg.drafted_tokens} slots submitted per step")
-
-    # Per-kernel split: the same projection through dspark_logits, then the
-    # chain through dspark_chain (the d2t and adaptive forms have no separate
-    # chain entry: their chain time is the step minus the projection).
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for e in evs:
-        e[0].record(stream)
-        dsp.logits(d["hidden"], d["lm_head"], layout=cfg.layout,
-                   lm_head_bias=None if args.d2t else d["lm_head_bias"], out=out.logits,
-                   stream=stream)
-        e[1].record(stream)
-        if not (args.d2t or args.adaptive):
-            dsp.chain(out.logits, d["markov_w1"], d["markov_w2"], d["anchors"], B=cfg.B, L=cfg.L,
-                      layout=cfg.layout, top_k=cfg.top_k, p_min=cfg.p_min, hidden=d["hidden"],
-                      conf_w=d["conf_w"], out=out, stream=stream)
-        e[2].record(stream)
-    torch.cuda.synchronize()
-    gemm_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    chain_ms = ((ms - gemm_ms) if (args.d2t or args.adaptive)
-                else sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps)
-    log(f"lm_head GEMM {gemm_ms * 1e3:.1f} us, chain+finalize {chain_ms * 1e3:.1f} us")
 
     # Greedy lattice verification of the step's proposal (dspark_verify), with
     # the target taken equal to the drafted chain: every submitted slot is
@@ -263,11 +324,19 @@ def main() -> int:
                        "submitted_per_step": submitted} if args.adaptive else {})},
         "roofline": {**gemm_roof,
                      "traffic": None if args.d2t else measured_traffic(cfg.name),
-                     "kernel": "lmhead_gemm", "us": gemm_ms * 1e3},
+                     "kernel": "lmhead_gemm", "us": gemm_ms * 1e3,
+                     "timed": "events around the projection inside the timed steps" if plain
+                              else "dspark_logits alone"},
         "roofline_chain": {"bound": "hbm", "achieved": chain_gbs, "peak": PEAK_HBM_GBS,
                            "unit": "GB/s", "frac": chain_gbs / PEAK_HBM_GBS,
-                           "bytes": chain_bytes, "kernels": "chain_init + chain_step x n_pred + finalize",
-                           "us": chain_ms * 1e3},
+                           "bytes": chain_bytes, "kernels": "chain_step x n_pred + finalize",
+                           "us": chain_ms * 1e3,
+                           **({"us_steps": phases["chain"] * 1e3,
+                               "us_finalize": phases["finalize"] * 1e3,
+                               "frac_steps": chain_bytes / (phases["chain"] * 1e-3) / 1e9 / PEAK_HBM_GBS}
+                              if plain else {})},
+        **({"phases_us": {k: v * 1e3 for k, v in phases.items()}} if plain else {}),
+        "unmarked_ms_per_step": ms_unmarked,
         "wall_ms_per_step": 1e3 * wall / args.steps,
         # call time of dspark_verify through the binding, host enqueue included
         # (its two kernels take a few microseconds: see the kernel statistics)
@@ -276,7 +345,7 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_blocks} blocks")
-        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_blocks)
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_blocks, args.cpu_single_blocks)
     print(json.dumps(res), flush=True)
     return 0
 

@@ -36,7 +36,8 @@ FLAG_BAD_D2T = 4
 MAX_TOP_K = 16
 MAX_RANK = 256
 
-EXPORTS = ("dspark_workspace_bytes", "dspark_propose", "dspark_logits", "dspark_chain",
+EXPORTS = ("dspark_workspace_bytes", "dspark_propose", "dspark_propose_marked", "dspark_logits",
+           "dspark_chain",
            "dspark_propose_d2t", "dspark_propose_adaptive", "dspark_verify", "dspark_read_flags",
            "dspark_status_string")
 
@@ -69,6 +70,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                    _i, _i, _i, _i, _i, _i, _i, _f,
                                    _vp, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.dspark_propose.restype = _i
+    lib.dspark_propose_marked.argtypes = lib.dspark_propose.argtypes + [_vp, _vp, _vp]
+    lib.dspark_propose_marked.restype = _i
     lib.dspark_logits.argtypes = [_vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]
     lib.dspark_logits.restype = _i
     lib.dspark_chain.argtypes = [_vp, _vp, _i, _vp, _vp, _vp, _vp,
@@ -172,10 +175,22 @@ class Outputs:
                 "cand_logits": self.cand_logits, "conf": self.conf, "lengths": self.lengths}
 
 
+def _event_handle(ev) -> Optional[int]:
+    """The hipEvent_t of a torch.cuda.Event (created by its first record)."""
+    if ev is None:
+        return None
+    if not ev.cuda_event:
+        ev.record()
+    return int(ev.cuda_event)
+
+
 def propose(hidden, lm_head, markov_w1, markov_w2, anchors, *, layout="anchor_first", top_k=1,
             p_min=0.0, lm_head_bias=None, conf_w=None, out: Optional[Outputs] = None,
-            stream=None) -> Outputs:
-    """Run dspark_propose on device tensors; returns the Outputs holding the results."""
+            stream=None, marks=None) -> Outputs:
+    """Run dspark_propose on device tensors; returns the Outputs holding the results.
+    With ``marks`` = (init, projected, chained) torch.cuda.Events (any may be
+    None) the call is dspark_propose_marked, which records them on the stream
+    between its launches."""
     torch = _torch()
     lib = load_library()
     B, L, H = hidden.shape
@@ -190,14 +205,17 @@ def propose(hidden, lm_head, markov_w1, markov_w2, anchors, *, layout="anchor_fi
     _check_dev("anchors", anchors, torch.int32, (B,))
     if out is None:
         out = Outputs(B, L, V, top_k, layout, hidden.device)
-    st = lib.dspark_propose(
-        _ptr(hidden), _hidden_dtype(hidden), _ptr(lm_head), _ptr(lm_head_bias), _ptr(markov_w1),
-        _ptr(markov_w2), _ptr(conf_w), _ptr(anchors), B, L, H, V, r, LAYOUTS[layout], top_k,
-        float(p_min), _ptr(out.logits), _ptr(out.workspace), out.workspace.numel(),
-        _ptr(out.tokens), _ptr(out.candidates), _ptr(out.cand_logits), _ptr(out.conf),
-        _ptr(out.lengths), _stream(hidden, stream))
+    args = (_ptr(hidden), _hidden_dtype(hidden), _ptr(lm_head), _ptr(lm_head_bias), _ptr(markov_w1),
+            _ptr(markov_w2), _ptr(conf_w), _ptr(anchors), B, L, H, V, r, LAYOUTS[layout], top_k,
+            float(p_min), _ptr(out.logits), _ptr(out.workspace), out.workspace.numel(),
+            _ptr(out.tokens), _ptr(out.candidates), _ptr(out.cand_logits), _ptr(out.conf),
+            _ptr(out.lengths), _stream(hidden, stream))
+    if marks is None:
+        st = lib.dspark_propose(*args)
+    else:
+        st = lib.dspark_propose_marked(*args, *[_event_handle(e) for e in marks])
     if st != OK:
-        raise DsparkError(st, "dspark_propose")
+        raise DsparkError(st, "dspark_propose_marked" if marks is not None else "dspark_propose")
     return out
 
 

@@ -61,6 +61,21 @@ __device__ __forceinline__ u64 make_key(float score, int id) {
 __device__ __forceinline__ int key_id(u64 key) { return (int)(~(uint32_t)key); }
 __device__ __forceinline__ float key_score(u64 key) { return unorder_f32((uint32_t)(key >> 32)); }
 
+// Largest value over the 32 lanes of this lane's half wave (lanes 0-31 or
+// 32-63), in every lane of the half: quad exchanges and row rotations (DPP),
+// then the other 16 lanes of the half (ds_swizzle, xor 16).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float half_wave_max(float v) {
+    v = fmaxf(v, dpp_f32<0xB1>(v));    // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp_f32<0x4E>(v));    // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp_f32<0x124>(v));   // row_ror:4
+    v = fmaxf(v, dpp_f32<0x128>(v));   // row_ror:8
+    return fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));
+}
+
 __device__ __forceinline__ u64 shfl_xor_u64(u64 v, int mask) {
     uint32_t lo = __shfl_xor((uint32_t)v, mask, kWave);
     uint32_t hi = __shfl_xor((uint32_t)(v >> 32), mask, kWave);

@@ -24,21 +24,31 @@ constexpr size_t kFlagsBytes = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t winners_off, partials_off, total;
+    size_t winners_off, bins_off, partials_off, total;
 };
 
-// [flags (256 B)] [winners: n_pred*kWinnerWays*winners_stride(B) u64]
+// [flags (256 B): flags word, gate's slot count, markov_w2 norm word]
+// [winners: n_pred*kWinnerWays*winners_stride(B) u64]
+// [bins: B*n_pred*kBoundBins u32, top_k > 1]
 // [partials: n_pred*B*nwg*top_k u64, top_k > 1]
 Layout workspace_layout(int B, int n_pred, int V, int top_k) {
     Layout l;
     l.winners_off = kFlagsBytes;
     const size_t win = align_up((size_t)n_pred * kWinnerWays * (size_t)winners_stride(B) * 8u);
-    l.partials_off = l.winners_off + win;
+    l.bins_off = l.winners_off + win;
+    const size_t bins = top_k > 1 ? align_up((size_t)B * n_pred * kBoundBins * 4u) : 0;
+    l.partials_off = l.bins_off + bins;
     const size_t part =
         top_k > 1 ? align_up((size_t)n_pred * B * (size_t)chain_workgroups_max(V) * top_k * 8u) : 0;
     l.total = l.partials_off + part;
     return l;
 }
+
+// Byte offsets of the words in the flags block.
+constexpr size_t kStopWord = 4, kW2NormWord = 8;
+// Extra workgroups of the projection that take the markov_w2 norm for the
+// top-k bound (they run in the projection's last, partly filled round).
+constexpr int kW2NormGroups = 64;
 
 int first_pred(int layout) { return layout == DSPARK_LAYOUT_BONUS_ANCHOR ? 1 : 0; }
 
@@ -87,25 +97,22 @@ struct ChainExtras {
     const int32_t* top_k_b = nullptr; // adaptive: candidates kept per block
 };
 
-// The chain over V columns.
-int run_chain(const float* logits, const void* hidden, int hidden_dtype, const uint16_t* w1,
-              const uint16_t* w2, const ChainExtras& x, const uint16_t* conf_w,
-              const int32_t* anchors, int B, int L, int H, int V, int r, int layout, int top_k,
-              float p_min, void* workspace, int32_t* tokens, int32_t* candidates,
-              float* cand_logits, float* conf, int32_t* lengths, hipStream_t stream) {
-    const int i_first = first_pred(layout);
-    const int n_pred = L - i_first;
+// Arguments of the chain kernels over V columns. With `bounded` (top_k > 1
+// only) the chain reads the top-k bound that the projection of the same
+// call leaves in the workspace.
+ChainArgs chain_args(const float* logits, const uint16_t* w1, const uint16_t* w2,
+                     const ChainExtras& x, const int32_t* anchors, int B, int L, int V, int r,
+                     int layout, int top_k, void* workspace, int32_t* lengths, bool bounded) {
+    const int n_pred = L - first_pred(layout);
     const Layout wl = workspace_layout(B, n_pred, V, top_k);
     char* ws = static_cast<char*>(workspace);
-
-    ChainArgs c;
+    ChainArgs c{};
     c.logits = logits;
     c.w1 = w1;
     c.w2 = w2;
     c.d2t = x.d2t;
     c.vocab = x.vocab > 0 ? x.vocab : V;
-    // the word after the flags word holds the gate's slot count
-    c.stop = x.p_min_b ? reinterpret_cast<const int32_t*>(ws + sizeof(uint32_t)) : nullptr;
+    c.stop = x.p_min_b ? reinterpret_cast<const int32_t*>(ws + kStopWord) : nullptr;
     c.anchors = anchors;
     c.winners = reinterpret_cast<unsigned long long*>(ws + wl.winners_off);
     c.partials = top_k > 1 ? reinterpret_cast<unsigned long long*>(ws + wl.partials_off) : nullptr;
@@ -118,9 +125,27 @@ int run_chain(const float* logits, const void* hidden, int hidden_dtype, const u
     c.top_k = top_k;
     c.nwg = chain_workgroups(B, V, r, top_k);
     c.wstride = winners_stride(B);
+    const bool bound = bounded && top_k > 1;
+    c.bins = bound ? reinterpret_cast<uint32_t*>(ws + wl.bins_off) : nullptr;
+    c.w2n2 = bound ? reinterpret_cast<uint32_t*>(ws + kW2NormWord) : nullptr;
+    return c;
+}
 
-    clear_pending_error();
-    hipError_t e = launch_chain_init(c, stream);
+// The chain over V columns (chain_init already enqueued when `initialised`).
+int run_chain(const ChainArgs& c, bool initialised, const void* hidden, int hidden_dtype,
+              const ChainExtras& x, const uint16_t* conf_w, int B, int L, int H, int V,
+              int layout, int top_k, float p_min, void* workspace, int32_t* tokens,
+              int32_t* candidates, float* cand_logits, float* conf, int32_t* lengths,
+              hipStream_t stream, hipEvent_t mark_chained = nullptr) {
+    const int i_first = first_pred(layout);
+    const int n_pred = L - i_first;
+    char* ws = static_cast<char*>(workspace);
+
+    hipError_t e = hipSuccess;
+    if (!initialised) {
+        clear_pending_error();
+        e = launch_chain_init(c, stream);
+    }
     if (e == hipSuccess && x.p_min_b) {
         GateArgs g;
         g.hidden = hidden;
@@ -128,7 +153,7 @@ int run_chain(const float* logits, const void* hidden, int hidden_dtype, const u
         g.p_min = x.p_min_b;
         g.conf = conf;
         g.lengths = lengths;
-        g.stop = reinterpret_cast<int32_t*>(ws + sizeof(uint32_t));
+        g.stop = reinterpret_cast<int32_t*>(ws + kStopWord);
         g.B = B;
         g.L = L;
         g.H = H;
@@ -138,6 +163,7 @@ int run_chain(const float* logits, const void* hidden, int hidden_dtype, const u
         e = launch_gate(g, stream);
     }
     for (int j = 0; j < n_pred && e == hipSuccess; ++j) e = launch_chain_step(c, j, stream);
+    if (e == hipSuccess && mark_chained) e = hipEventRecord(mark_chained, stream);
     if (e != hipSuccess) return DSPARK_ERR_HIP;
 
     FinalArgs f;
@@ -168,6 +194,78 @@ int run_chain(const float* logits, const void* hidden, int hidden_dtype, const u
     return hip_status(launch_finalize(f, stream));
 }
 
+GemmArgs gemm_args(const void* hidden, const uint16_t* lm_head, const float* bias, int B, int L,
+                   int H, int V, int layout, float* logits, const ChainArgs* c, int r) {
+    GemmArgs g{};
+    g.hidden = hidden;
+    g.lm_head = lm_head;
+    g.bias = bias;
+    g.out = logits;
+    g.i_first = first_pred(layout);
+    g.n_pred = L - g.i_first;
+    g.M = B * g.n_pred;
+    g.N = V;
+    g.K = H;
+    g.L = L;
+    if (c != nullptr && c->bins != nullptr) {
+        g.bins = c->bins;
+        if (r > 0) {
+            g.w2 = c->w2;
+            g.w2_rows = V;
+            g.w2_rank = r;
+            g.w2n2 = c->w2n2;
+            g.w2_groups = kW2NormGroups;
+        }
+    }
+    return g;
+}
+
+// chain_init (which zeroes the bins and the norm word), then the projection
+// with the bound's epilogue when the chain is bounded.
+int project(const ChainArgs& c, const void* hidden, int hidden_dtype, const uint16_t* lm_head,
+            const float* bias, int B, int L, int H, int V, int layout, float* logits,
+            hipStream_t stream, hipEvent_t mark_init = nullptr, hipEvent_t mark_projected = nullptr) {
+    clear_pending_error();
+    hipError_t e = launch_chain_init(c, stream);
+    if (e == hipSuccess && mark_init) e = hipEventRecord(mark_init, stream);
+    if (e == hipSuccess)
+        e = launch_lmhead_gemm(gemm_args(hidden, lm_head, bias, B, L, H, V, layout, logits, &c, c.r),
+                               hidden_dtype == DSPARK_HIDDEN_F32, stream);
+    if (e == hipSuccess && mark_projected) e = hipEventRecord(mark_projected, stream);
+    return hip_status(e);
+}
+
+int propose_impl(const void* hidden, int hidden_dtype, const uint16_t* lm_head,
+                 const float* lm_head_bias, const uint16_t* markov_w1, const uint16_t* markov_w2,
+                 const uint16_t* conf_w, const int32_t* anchors, int B, int L, int H, int V, int r,
+                 int layout, int top_k, float p_min, float* logits, void* workspace,
+                 size_t workspace_bytes, int32_t* tokens, int32_t* candidates, float* cand_logits,
+                 float* conf, int32_t* lengths, hipStream_t s, hipEvent_t mark_init,
+                 hipEvent_t mark_projected, hipEvent_t mark_chained) {
+    int st = check_sizes(B, L, H, V, layout, hidden_dtype);
+    if (st != DSPARK_OK) return st;
+    st = check_chain_args(V, r, top_k, p_min, markov_w1, markov_w2);
+    if (st != DSPARK_OK) return st;
+    if (!hidden || !lm_head || !logits || !anchors || !tokens || !candidates || !lengths)
+        return DSPARK_ERR_INVALID_ARG;
+    if (!aligned16(hidden) || !aligned16(lm_head) || !aligned16(logits) ||
+        (conf_w && !aligned16(conf_w)))
+        return DSPARK_ERR_UNSUPPORTED;
+    if (!workspace) return DSPARK_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return DSPARK_ERR_WORKSPACE;
+    const int n_pred = L - first_pred(layout);
+    if (workspace_bytes < workspace_layout(B, n_pred, V, top_k).total) return DSPARK_ERR_WORKSPACE;
+
+    const ChainArgs c = chain_args(logits, markov_w1, markov_w2, ChainExtras(), anchors, B, L, V, r,
+                                   layout, top_k, workspace, lengths, true);
+    st = project(c, hidden, hidden_dtype, lm_head, lm_head_bias, B, L, H, V, layout, logits, s,
+                 mark_init, mark_projected);
+    if (st != DSPARK_OK) return st;
+    return run_chain(c, true, hidden, hidden_dtype, ChainExtras(), conf_w, B, L, H, V, layout, top_k,
+                     p_min, workspace, tokens, candidates, cand_logits, conf, lengths, s,
+                     mark_chained);
+}
+
 }  // namespace
 
 extern "C" {
@@ -187,20 +285,10 @@ int dspark_logits(const void* hidden, int hidden_dtype, const uint16_t* lm_head,
     if (st != DSPARK_OK) return st;
     if (!hidden || !lm_head || !logits) return DSPARK_ERR_INVALID_ARG;
     if (!aligned16(hidden) || !aligned16(lm_head)) return DSPARK_ERR_UNSUPPORTED;
-    const int i_first = first_pred(layout);
-    GemmArgs g;
-    g.hidden = hidden;
-    g.lm_head = lm_head;
-    g.bias = lm_head_bias;
-    g.out = logits;
-    g.n_pred = L - i_first;
-    g.M = B * g.n_pred;
-    g.N = V;
-    g.K = H;
-    g.L = L;
-    g.i_first = i_first;
     clear_pending_error();
-    return hip_status(launch_lmhead_gemm(g, hidden_dtype == DSPARK_HIDDEN_F32,
+    return hip_status(launch_lmhead_gemm(gemm_args(hidden, lm_head, lm_head_bias, B, L, H, V, layout,
+                                                   logits, nullptr, 0),
+                                         hidden_dtype == DSPARK_HIDDEN_F32,
                                          static_cast<hipStream_t>(stream)));
 }
 
@@ -221,9 +309,12 @@ int dspark_chain(const float* logits, const void* hidden, int hidden_dtype,
     if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return DSPARK_ERR_WORKSPACE;
     if (workspace_bytes < dspark_workspace_bytes(B, L, V, top_k, layout)) return DSPARK_ERR_WORKSPACE;
     if (!aligned16(logits)) return DSPARK_ERR_UNSUPPORTED;
-    return run_chain(logits, hidden, hidden_dtype, markov_w1, markov_w2, ChainExtras(), conf_w,
-                     anchors, B, L, H, V, r, layout, top_k, p_min, workspace, tokens, candidates,
-                     cand_logits, conf, lengths, static_cast<hipStream_t>(stream));
+    // caller projections: no bound from a projection of this call
+    const ChainArgs c = chain_args(logits, markov_w1, markov_w2, ChainExtras(), anchors, B, L, V, r,
+                                   layout, top_k, workspace, lengths, false);
+    return run_chain(c, false, hidden, hidden_dtype, ChainExtras(), conf_w, B, L, H, V, layout, top_k,
+                     p_min, workspace, tokens, candidates, cand_logits, conf, lengths,
+                     static_cast<hipStream_t>(stream));
 }
 
 int dspark_propose(const void* hidden, int hidden_dtype, const uint16_t* lm_head,
@@ -233,25 +324,25 @@ int dspark_propose(const void* hidden, int hidden_dtype, const uint16_t* lm_head
                    float* logits, void* workspace, size_t workspace_bytes, int32_t* tokens,
                    int32_t* candidates, float* cand_logits, float* conf, int32_t* lengths,
                    void* stream) {
-    int st = check_sizes(B, L, H, V, layout, hidden_dtype);
-    if (st != DSPARK_OK) return st;
-    st = check_chain_args(V, r, top_k, p_min, markov_w1, markov_w2);
-    if (st != DSPARK_OK) return st;
-    if (!hidden || !lm_head || !logits || !anchors || !tokens || !candidates || !lengths)
-        return DSPARK_ERR_INVALID_ARG;
-    if (!aligned16(hidden) || !aligned16(lm_head) || !aligned16(logits) ||
-        (conf_w && !aligned16(conf_w)))
-        return DSPARK_ERR_UNSUPPORTED;
-    if (!workspace) return DSPARK_ERR_WORKSPACE;
-    if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return DSPARK_ERR_WORKSPACE;
-    if (workspace_bytes < dspark_workspace_bytes(B, L, V, top_k, layout)) return DSPARK_ERR_WORKSPACE;
+    return propose_impl(hidden, hidden_dtype, lm_head, lm_head_bias, markov_w1, markov_w2, conf_w,
+                        anchors, B, L, H, V, r, layout, top_k, p_min, logits, workspace,
+                        workspace_bytes, tokens, candidates, cand_logits, conf, lengths,
+                        static_cast<hipStream_t>(stream), nullptr, nullptr, nullptr);
+}
 
-    st = dspark_logits(hidden, hidden_dtype, lm_head, lm_head_bias, B, L, H, V, layout, logits,
-                       stream);
-    if (st != DSPARK_OK) return st;
-    return run_chain(logits, hidden, hidden_dtype, markov_w1, markov_w2, ChainExtras(), conf_w,
-                     anchors, B, L, H, V, r, layout, top_k, p_min, workspace, tokens, candidates,
-                     cand_logits, conf, lengths, static_cast<hipStream_t>(stream));
+int dspark_propose_marked(const void* hidden, int hidden_dtype, const uint16_t* lm_head,
+                          const float* lm_head_bias, const uint16_t* markov_w1,
+                          const uint16_t* markov_w2, const uint16_t* conf_w,
+                          const int32_t* anchors, int B, int L, int H, int V, int r, int layout,
+                          int top_k, float p_min, float* logits, void* workspace,
+                          size_t workspace_bytes, int32_t* tokens, int32_t* candidates,
+                          float* cand_logits, float* conf, int32_t* lengths, void* stream,
+                          void* mark_init, void* mark_projected, void* mark_chained) {
+    return propose_impl(hidden, hidden_dtype, lm_head, lm_head_bias, markov_w1, markov_w2, conf_w,
+                        anchors, B, L, H, V, r, layout, top_k, p_min, logits, workspace,
+                        workspace_bytes, tokens, candidates, cand_logits, conf, lengths,
+                        static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(mark_init),
+                        static_cast<hipEvent_t>(mark_projected), static_cast<hipEvent_t>(mark_chained));
 }
 
 int dspark_propose_d2t(const void* hidden, int hidden_dtype, const uint16_t* lm_head,
@@ -277,14 +368,16 @@ int dspark_propose_d2t(const void* hidden, int hidden_dtype, const uint16_t* lm_
     if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return DSPARK_ERR_WORKSPACE;
     if (workspace_bytes < dspark_workspace_bytes(B, L, D, top_k, layout)) return DSPARK_ERR_WORKSPACE;
 
-    st = dspark_logits(hidden, hidden_dtype, lm_head, nullptr, B, L, H, D, layout, logits, stream);
-    if (st != DSPARK_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
     ChainExtras x;
     x.d2t = d2t;
     x.vocab = V;
-    return run_chain(logits, hidden, hidden_dtype, markov_w1, markov_w2, x, conf_w, anchors, B, L,
-                     H, D, r, layout, top_k, p_min, workspace, tokens, candidates, cand_logits,
-                     conf, lengths, static_cast<hipStream_t>(stream));
+    const ChainArgs c = chain_args(logits, markov_w1, markov_w2, x, anchors, B, L, D, r, layout,
+                                   top_k, workspace, lengths, true);
+    st = project(c, hidden, hidden_dtype, lm_head, nullptr, B, L, H, D, layout, logits, s);
+    if (st != DSPARK_OK) return st;
+    return run_chain(c, true, hidden, hidden_dtype, x, conf_w, B, L, H, D, layout, top_k, p_min,
+                     workspace, tokens, candidates, cand_logits, conf, lengths, s);
 }
 
 int dspark_propose_adaptive(const void* hidden, int hidden_dtype, const uint16_t* lm_head,
@@ -308,15 +401,16 @@ int dspark_propose_adaptive(const void* hidden, int hidden_dtype, const uint16_t
     if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return DSPARK_ERR_WORKSPACE;
     if (workspace_bytes < dspark_workspace_bytes(B, L, V, top_k, layout)) return DSPARK_ERR_WORKSPACE;
 
-    st = dspark_logits(hidden, hidden_dtype, lm_head, lm_head_bias, B, L, H, V, layout, logits,
-                       stream);
-    if (st != DSPARK_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
     ChainExtras x;
     x.p_min_b = p_min;
     x.top_k_b = block_top_k;
-    return run_chain(logits, hidden, hidden_dtype, markov_w1, markov_w2, x, conf_w, anchors, B, L,
-                     H, V, r, layout, top_k, 0.0f, workspace, tokens, candidates, cand_logits,
-                     conf, lengths, static_cast<hipStream_t>(stream));
+    const ChainArgs c = chain_args(logits, markov_w1, markov_w2, x, anchors, B, L, V, r, layout,
+                                   top_k, workspace, lengths, true);
+    st = project(c, hidden, hidden_dtype, lm_head, lm_head_bias, B, L, H, V, layout, logits, s);
+    if (st != DSPARK_OK) return st;
+    return run_chain(c, true, hidden, hidden_dtype, x, conf_w, B, L, H, V, layout, top_k, 0.0f,
+                     workspace, tokens, candidates, cand_logits, conf, lengths, s);
 }
 
 int dspark_verify(const int32_t* candidates, const int32_t* lengths, const int32_t* target, int B,

@@ -8,6 +8,15 @@
 namespace dspark {
 
 // ---- lm_head projection ---------------------------------------------------
+// Row-maximum bins: a lower bound on the top-k scores of every chain slot,
+// produced by the projection's epilogue. The columns of a row are cut into
+// slabs (the columns one wave of a tile holds); slab s raises bin
+// s % kBoundBins of row m to the largest projection of the row over the
+// slab's columns (as an order_f32 key; 0 = no column yet). The bins partition
+// the columns, so every non-empty bin is the projection of a distinct column:
+// the k-th largest bin is at most the k-th largest projection of the row.
+constexpr int kBoundBins = 16;
+
 struct GemmArgs {
     const void* hidden;      // [B, L, H] bf16 bits or fp32
     const uint16_t* lm_head; // [V, H] bf16 bits
@@ -15,6 +24,13 @@ struct GemmArgs {
     float* out;              // [M, V], M = B * n_pred
     int M, N, K;             // M rows, N = V, K = H
     int L, n_pred, i_first;  // row m reads hidden row (m / n_pred) * L + i_first + m % n_pred
+    uint32_t* bins;          // [M, kBoundBins] row-maximum bins (zeroed before), or nullptr
+    // With bins: the largest squared row norm of markov_w2 [w2_rows, w2_rank]
+    // is raised into *w2n2 (fp32 bits, zeroed before) by w2_groups extra
+    // workgroups after the tiles of the launch (they run in its last round).
+    const uint16_t* w2;
+    int w2_rows, w2_rank, w2_groups;
+    uint32_t* w2n2;
 };
 hipError_t launch_lmhead_gemm(const GemmArgs& a, bool hidden_f32, hipStream_t stream);
 
@@ -118,7 +134,14 @@ struct ChainArgs {
     int wstride;               // winners_stride(B)
     int vocab;                 // target vocabulary size (== V without d2t)
     const int32_t* stop;       // adaptive gate: slots from *stop on are skipped (nullptr: none)
+    // Top-k bound (top_k > 1, after a projection that filled them), or nullptr:
+    // bins [B * n_pred, kBoundBins] (GemmArgs) and the largest squared row
+    // norm of markov_w2 (fp32 bits).
+    uint32_t* bins;
+    uint32_t* w2n2;
 };
+// Zeroes the running-argmax words, the flags, the bins and *w2n2 (when
+// present) and presets lengths to n_pred; enqueued before the projection.
 hipError_t launch_chain_init(const ChainArgs& a, hipStream_t stream);
 hipError_t launch_chain_step(const ChainArgs& a, int j, hipStream_t stream);
 

@@ -31,6 +31,62 @@ constexpr int BK = 64;
 // non-temporal: the logits are streamed out once and should not evict the
 // lm_head / hidden tiles from L2. The bias is read once per column before any
 // store, and tiles that lie wholly inside the matrix store without predicates.
+// An extra workgroup g (of a.w2_groups, numbered after the tiles) of a
+// projection launch: the largest squared row norm of markov_w2 over rows
+// g * T + t, (g + G) * T + t, ... (T threads), a sum of squares of bf16 values
+// in fp32 (every square is exact), raised into *w2n2 as fp32 bits (the bits
+// of non-negative floats order as unsigned integers).
+__device__ __forceinline__ void w2_norm_part(const GemmArgs& a, int g) {
+    const int nt = blockDim.x, tid = threadIdx.x, r = a.w2_rank;
+    float best = 0.0f;
+    for (long row = (long)g * nt + tid; row < a.w2_rows; row += (long)a.w2_groups * nt) {
+        const uint16_t* p = a.w2 + row * r;
+        float s = 0.0f;
+        for (int k = 0; k < r; k += 8) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(p + k);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float lo = bf16_lo(w[q]), hi = bf16_hi(w[q]);
+                s += lo * lo;
+                s += hi * hi;
+            }
+        }
+        best = fmaxf(best, s);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) best = fmaxf(best, __shfl_xor(best, m, kWave));
+    if ((tid & 63) == 0) atomicMax(a.w2n2, __float_as_uint(best));
+}
+
+// Row-maximum bins (kernels.hpp, kBoundBins) of a wave's FM x FN block in
+// the plain accumulator layout: the lane holds column nb + 32 j + lane % 32
+// and, in register g, row mb + 32 i + acc_row(g, lane). The wave's columns
+// form one slab. Per row: the largest projection over the lane's columns,
+// then over the 32 lanes of the half wave; lane g of each half raises the
+// bin of the half's row g.
+template <int FM, int FN>
+__device__ __forceinline__ void row_bins(const GemmArgs& a, const f32x16 (&acc)[FM][FN],
+                                         const float (&bn)[FN], int mb, int nb, int slab_cols, int lane) {
+    if (nb >= a.N) return;   // no column of this wave's slab exists
+    const int lrow = lane & 31;
+    uint32_t* bin = a.bins + (nb / slab_cols) % kBoundBins;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        float pick = -INFINITY;
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+            float v = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                if (nb + j * 32 + lrow < a.N) v = fmaxf(v, acc[i][j][g] + bn[j]);
+            v = half_wave_max(v);
+            pick = lrow == g ? v : pick;
+        }
+        const int m = mb + i * 32 + acc_row(lrow, lane);
+        if (lrow < 16 && m < a.M) atomicMax(bin + (long)m * kBoundBins, order_f32(pick));
+    }
+}
+
 template <int BM, int BN, int WM, int WN>
 __device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x16 (&acc)[BM / WM / 32][BN / WN / 32],
                                            int m0, int n0, int wm, int wn, int lane) {
@@ -46,6 +102,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x16 (&acc
     // The bias loads must be complete before the first store: otherwise the
     // wait inserted for them also waits for every store issued so far.
     __builtin_amdgcn_s_waitcnt(0);
+    if (a.bins != nullptr) row_bins<FM, FN>(a, acc, bn, m0 + wm * TM, n0 + wn * TN, TN, lane);
     if (m0 + BM <= M && n0 + BN <= N) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
@@ -105,6 +162,10 @@ __global__ __launch_bounds__(64 * WM * WN) void lmhead_gemm(GemmArgs a) {
     const int M = a.M, N = a.N, K = a.K;
     const int nMT = (M + BM - 1) / BM, nNT = (N + BN - 1) / BN, T = nMT * nNT;
     const int bid = blockIdx.x;
+    if (bid >= T) {
+        w2_norm_part(a, bid - T);
+        return;
+    }
     // XCD-aware order: dispatch sends block i to XCD i % 8; give each XCD a
     // contiguous run of tiles, M fastest, so the M tiles of an N slab share an L2.
     const int sid = (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
@@ -259,6 +320,10 @@ __global__ __launch_bounds__(64 * WM * WN) void lmhead_gemm_dma(GemmArgs a) {
     const int M = a.M, N = a.N, K = a.K;
     const int nMT = (M + BM - 1) / BM, nNT = (N + BN - 1) / BN, T = nMT * nNT;
     const int bid = blockIdx.x;
+    if (bid >= T) {
+        w2_norm_part(a, bid - T);
+        return;
+    }
     const int sid = (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
     const int m0 = (sid % nMT) * BM, n0 = (sid / nMT) * BN;
 
@@ -379,6 +444,10 @@ __global__ __launch_bounds__(256) void lmhead_gemm_w4(GemmArgs a) {
     const int M = a.M, N = a.N, K = a.K;
     const int nMT = (M + BM - 1) / BM, nNT = (N + BN - 1) / BN, T = nMT * nNT;
     const int bid = blockIdx.x;
+    if (bid >= T) {
+        w2_norm_part(a, bid - T);
+        return;
+    }
     const int sid = (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
     const int m0 = (sid % nMT) * BM, n0 = (sid / nMT) * BN;
     const int lane = threadIdx.x & 63;
@@ -528,9 +597,14 @@ __global__ __launch_bounds__(256) void lmhead_gemm_w4(GemmArgs a) {
     store_tile<BM, BN, 2, 2>(a, acc, m0, n0, wm, wn, lane);
 }
 
+// Workgroups of a launch: the tiles, then the markov_w2 norm groups.
+long launch_groups(const GemmArgs& a, int BM, int BN) {
+    return (long)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) + (a.w2n2 != nullptr ? a.w2_groups : 0);
+}
+
 template <int BM, int BN, int WM, int WN, int NS, int BKS = 32>
 hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
-    const long tiles = (long)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+    const long tiles = launch_groups(a, BM, BN);
     if (tiles > 0x7fffffffL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((lmhead_gemm_dma<BM, BN, WM, WN, NS, BKS>), dim3((unsigned)tiles),
                        dim3(64 * WM * WN), 0, s, a);
@@ -539,7 +613,7 @@ hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
 
 template <int BM, int BN, int WM, int WN>
 hipError_t launch_cfg(const GemmArgs& a, bool f32, hipStream_t s) {
-    const long tiles = (long)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+    const long tiles = launch_groups(a, BM, BN);
     if (tiles > 0x7fffffffL) return hipErrorInvalidValue;
     dim3 grid((unsigned)tiles), block(64 * WM * WN);
     const bool kfull = a.K % BK == 0;
@@ -562,7 +636,7 @@ hipError_t launch_lmhead_gemm(const GemmArgs& a, bool hidden_f32, hipStream_t st
         // must each span less than 4 GiB
         const long hid_bytes = (long)((a.M + a.n_pred - 1) / a.n_pred) * a.L * a.K * 2;
         if (a.M > 128 && a.K % 64 == 0 && hid_bytes < 0xFFFFFFFFL && 256L * a.K * 2 < 0x7FFFFFFFL) {
-            const long tiles = (long)((a.M + 255) / 256) * ((a.N + 255) / 256);
+            const long tiles = launch_groups(a, 256, 256);
             if (tiles > 0x7fffffffL) return hipErrorInvalidValue;
             hipLaunchKernelGGL(lmhead_gemm_w4, dim3((unsigned)tiles), dim3(256), 0, stream, a);
             return hipGetLastError();

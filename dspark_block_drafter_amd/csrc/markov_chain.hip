@@ -35,11 +35,16 @@ constexpr int kWaves = 4;
 static_assert(kChainTileV == kWaves * 32, "one 32-column block per wave");
 
 __global__ __launch_bounds__(256) void chain_init(u64* winners, int n, uint32_t* flags,
-                                                  int32_t* lengths, int B, int n_pred) {
+                                                  int32_t* lengths, int B, int n_pred,
+                                                  uint32_t* bins, int nbins, uint32_t* w2n2) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) winners[i] = 0ull;
     if (i < B) lengths[i] = n_pred;
-    if (i == 0) *flags = 0u;
+    if (i < nbins) bins[i] = 0u;
+    if (i == 0) {
+        *flags = 0u;
+        if (w2n2) *w2n2 = 0u;
+    }
 }
 
 // ---- pieces shared by the two step kernels ----------------------------------
@@ -154,6 +159,72 @@ __device__ __forceinline__ void publish(const ChainArgs& a, int j, int bbase, u6
     }
 }
 
+// ---- top-k bound from the projection's row-maximum bins ----------------------
+
+// Lower bound on the KL-th best biased score of one slot of one block, from
+// which its top-k filter starts. The KL largest row-maximum bins are the
+// projections of KL distinct columns of the row (kernels.hpp, kBoundBins);
+// the Markov term of any column is at most |markov_w2[v]| |u| in magnitude
+// (Cauchy-Schwarz, u = markov_w1[prev]), so those KL columns score at least
+// kth - |w2|max |u|. The scores are fp32 sums of r + 1 terms, within
+// (r + 1) 2^-24 (|z| + |bias|) of exact (r <= 256: below 2e-5 relative), and
+// the norms carry a few ulps: the margins below cover both. -inf when fewer
+// than KL bins are set (a row with fewer slabs than KL).
+template <int KL>
+__device__ __forceinline__ float chain_bound(const uint32_t (&kb)[kBoundBins], float w2n2, float un2) {
+    uint32_t top[KL];
+#pragma unroll
+    for (int i = 0; i < KL; ++i) top[i] = 0u;
+#pragma unroll
+    for (int t = 0; t < kBoundBins; ++t) {
+        uint32_t x = kb[t];
+#pragma unroll
+        for (int i = 0; i < KL; ++i) {   // insertion into the decreasing list
+            const uint32_t hi = x > top[i] ? x : top[i];
+            x = x > top[i] ? top[i] : x;
+            top[i] = hi;
+        }
+    }
+    if (top[KL - 1] == 0u) return -INFINITY;
+    const float kth = unorder_f32(top[KL - 1]);
+    const float mk = sqrtf(w2n2) * sqrtf(un2);
+    return kth - mk * 1.001f - 1e-4f * (1.0f + fabsf(kth));
+}
+
+// Squared norm of this lane's block's markov_w1 row from its MFMA B-operand
+// share (rank chunks 16 s + 8 (lane / 32) .. + 8) and its partner lane's.
+template <int RS>
+__device__ __forceinline__ float w1_norm2(const u32x4 (&u)[RS > 0 ? RS : 1]) {
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < RS; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float lo = bf16_lo(u[i][q]), hi = bf16_hi(u[i][q]);
+            s += lo * lo;
+            s += hi * hi;
+        }
+    return s + __shfl_xor(s, 32, kWave);
+}
+
+// Direct-to-LDS copy of the bins of slot j of blocks bbase .. bbase + NBL - 1
+// (rows past B repeat block B - 1) into s_bins[NBL][kBoundBins], and of the
+// markov_w2 norm word into all 64 words of s_w2n2; issued by the first
+// NBL / 16 waves (64 lanes x 16 bytes each) and the last wave.
+template <int NBL>
+__device__ __forceinline__ void load_bound(const ChainArgs& a, int j, int bbase, uint32_t (*s_bins)[kBoundBins],
+                                           uint32_t* s_w2n2, int wave, int lane) {
+    static_assert(NBL % 16 == 0 && NBL / 16 <= kWaves, "one 16-byte copy per lane");
+    if (wave < NBL / 16) {
+        const int c = wave * 64 + lane, blk = c >> 2, part = c & 3;
+        const int b = min(bbase + blk, a.B - 1);
+        const uint32_t* src = a.bins + ((long)b * a.n_pred + j) * kBoundBins + part * 4;
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)&s_bins[wave * 16][0], 16, 0, 0);
+    }
+    if (wave == kWaves - 1)
+        __builtin_amdgcn_global_load_lds((const void*)a.w2n2, (lds_ptr)s_w2n2, 4, 0, 0);
+}
+
 // ---- step kernel for V % 4 == 0: operands staged through LDS -----------------
 
 // Swizzle of a staged row of R 16-byte chunks: chunk c of row `row` is stored
@@ -196,6 +267,10 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
     // block's KL-th best score in this workgroup, shared with the waves that
     // score the other columns of the same blocks.
     __shared__ float s_thr[kWaves][32];
+    // Row-maximum bins of the slot's blocks and the markov_w2 norm word (the
+    // top-k bound), copied in by the prologue.
+    __shared__ uint32_t s_bins[KL > 1 ? NB * 32 : 1][kBoundBins];
+    __shared__ uint32_t s_w2n2[64];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lrow = lane & 31, lhalf = lane >> 5;
@@ -203,6 +278,10 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
     // adaptive gate: every block was cut before this slot
     if (a.stop && j >= *a.stop) return;
     const int bbase = blockIdx.y * NB * 32;
+    // the bound's copies go first: the prologue's waits cover them
+    const bool bounded = KL > 1 && a.bins != nullptr;
+    if constexpr (KL > 1)
+        if (bounded) load_bound<NB * 32>(a, j, bbase, s_bins, s_w2n2, wave, lane);
     const int B = a.B, V = a.V, r = a.r;
     const int nT = (V + TS - 1) / TS, G = gridDim.x, g = blockIdx.x;
     const int t0 = (int)((long)nT * g / G), t1 = (int)((long)nT * (g + 1) / G);
@@ -312,6 +391,7 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
 #pragma unroll
     for (int i = 0; i < KL; ++i) list[i] = 0ull;
     if (lhalf == 0) s_thr[wave][lrow] = -INFINITY;
+    float tau = -INFINITY;   // the block's top-k bound (set once u is read)
 
     // Software pipeline over tiles: the bias product of tile it + 1 (LDS
     // reads + MFMA) is issued before the top-k work of tile it, so the matrix
@@ -347,8 +427,9 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
         for (int e = 0; e < 16; ++e) z[e] = sc.acc[e];
         const int vlane = vt + 4 * lhalf;
         const bool full = vt + 32 <= V;
-        if (!full || (KL > 1 && it == 0)) {
-            // plain inserts (the ragged last tile; the first tile of top-k lists)
+        if (!full || (KL > 1 && it == 0 && !bounded)) {
+            // plain inserts (the ragged last tile; the first tile of top-k
+            // lists when no bound is known)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int v = vlane + 8 * (e >> 2) + (e & 3);
@@ -387,6 +468,7 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
             float thr = fmaxf(sa[KL - 1], sb[KL - 1]);
 #pragma unroll
             for (int i = 1; i < KL; ++i) thr = fmaxf(thr, fminf(sa[i - 1], sb[KL - 1 - i]));
+            thr = fmaxf(thr, tau);
             if (lhalf == 0) s_thr[wave][lrow] = thr;
 #pragma unroll
             for (int w = 0; w < VW; ++w) thr = fmaxf(thr, s_thr[nbw * VW + w][lrow]);
@@ -458,6 +540,15 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
         for (int s = 0; s < RS; ++s) {
             u[s] = ring[NS - 1][(nbw * RS + s) * 64 + lane];
             if (s * 16 + lhalf * 8 >= r) u[s] = u32x4{0u, 0u, 0u, 0u};
+        }
+        if constexpr (KL > 1) {
+            if (bounded) {
+                const float un2 = w1_norm2<RS>(u);
+                uint32_t kb[kBoundBins];
+#pragma unroll
+                for (int t = 0; t < kBoundBins; ++t) kb[t] = s_bins[nbw * 32 + lrow][t];
+                tau = chain_bound<KL>(kb, __uint_as_float(s_w2n2[0]), un2);
+            }
         }
         score(0, S0);
     }
@@ -559,6 +650,10 @@ __global__ __launch_bounds__(256) void chain_step_wave(ChainArgs a, int j) {
     __shared__ u32x4 ring[kWaves][NS][STAGE];
     // Top-k bound of each wave's lane pairs, per block (see consume below).
     __shared__ float s_thr[kWaves][32];
+    // Row-maximum bins of the slot's blocks and the markov_w2 norm word (the
+    // top-k bound).
+    __shared__ uint32_t s_bins[KL > 1 ? NB * 32 : 1][kBoundBins];
+    __shared__ uint32_t s_w2n2[64];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -566,6 +661,9 @@ __global__ __launch_bounds__(256) void chain_step_wave(ChainArgs a, int j) {
     const int vb = wave % VW, nbw = wave / VW;
     if (a.stop && j >= *a.stop) return;   // adaptive gate: every block was cut
     const int bbase = blockIdx.y * NB * 32;
+    const bool bounded = KL > 1 && a.bins != nullptr;
+    if constexpr (KL > 1)
+        if (bounded) load_bound<NB * 32>(a, j, bbase, s_bins, s_w2n2, wave, lane);
     const int B = a.B, V = a.V, r = a.r;
     const int nT = (V + TS - 1) / TS, G = gridDim.x, g = blockIdx.x;
     const int t0 = (int)((long)nT * g / G), t1 = (int)((long)nT * (g + 1) / G);
@@ -632,6 +730,7 @@ __global__ __launch_bounds__(256) void chain_step_wave(ChainArgs a, int j) {
     const int prev = active ? prev_token(a, j, bme, vb == 0) : 0;
     if (lhalf == 0) s_thr[wave][lrow] = -INFINITY;
     wait_lds_reads();
+    if (bounded) wait_vmcnt<0>();   // the bound's copies (and the previous tokens)
     block_barrier();   // every bound is set before any wave reads it
 
     // Tile 0, the markov_w1 rows of prev (the MFMA B operand) into stage
@@ -658,6 +757,16 @@ __global__ __launch_bounds__(256) void chain_step_wave(ChainArgs a, int j) {
     for (int s = 0; s < RS; ++s) {
         u[s] = ring[wave][NS - 1][s * 64 + lane];
         if (s * 16 + lhalf * 8 >= r) u[s] = u32x4{0u, 0u, 0u, 0u};
+    }
+    float tau = -INFINITY;   // the block's top-k bound
+    if constexpr (KL > 1) {
+        if (bounded) {
+            const float un2 = w1_norm2<RS>(u);
+            uint32_t kb[kBoundBins];
+#pragma unroll
+            for (int t = 0; t < kBoundBins; ++t) kb[t] = s_bins[nbw * 32 + lrow][t];
+            tau = chain_bound<KL>(kb, __uint_as_float(s_w2n2[0]), un2);
+        }
     }
     asm volatile("" ::: "memory");
     wait_lds_reads();
@@ -700,9 +809,9 @@ __global__ __launch_bounds__(256) void chain_step_wave(ChainArgs a, int j) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) z[e] = acc[e];
         const int vlane = vt + 4 * lhalf;
-        if (vt + 32 > V || (KL > 1 && it == 0)) {
+        if (vt + 32 > V || (KL > 1 && it == 0 && !bounded)) {
             // plain inserts of the columns inside V (the ragged last tile;
-            // the first step of top-k lists)
+            // the first step of top-k lists when no bound is known)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int v = vlane + 8 * (e >> 2) + (e & 3);
@@ -740,6 +849,7 @@ __global__ __launch_bounds__(256) void chain_step_wave(ChainArgs a, int j) {
             float thr = fmaxf(sa[KL - 1], sb[KL - 1]);
 #pragma unroll
             for (int i = 1; i < KL; ++i) thr = fmaxf(thr, fminf(sa[i - 1], sb[KL - 1 - i]));
+            thr = fmaxf(thr, tau);
             if (lhalf == 0 && active) s_thr[wave][lrow] = thr;
 #pragma unroll
             for (int w = 0; w < VW; ++w)
@@ -1185,9 +1295,11 @@ hipError_t step_kl(const ChainArgs& a, int j, dim3 grid, ChainForm f, hipStream_
 
 hipError_t launch_chain_init(const ChainArgs& a, hipStream_t stream) {
     const int nw = a.n_pred * kWinnerWays * a.wstride;   // < 2^31 (checked on the host)
-    const int n = nw > a.B ? nw : a.B;
+    const int nb = a.bins ? a.B * a.n_pred * kBoundBins : 0;
+    int n = nw > a.B ? nw : a.B;
+    n = n > nb ? n : nb;
     hipLaunchKernelGGL(chain_init, dim3((n + 255) / 256), dim3(256), 0, stream, a.winners, nw,
-                       a.flags, a.lengths, a.B, a.n_pred);
+                       a.flags, a.lengths, a.B, a.n_pred, a.bins, nb, a.w2n2);
     return hipGetLastError();
 }
 

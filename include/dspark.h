@@ -104,9 +104,11 @@ typedef enum {
 /*
  * Bytes of device workspace that dspark_propose / dspark_chain need for these
  * sizes (pure host function, no HIP call). Returns 0 if the sizes are invalid.
- * The workspace holds the per-slot running argmax words, the per-workgroup
- * top-k partial lists (top_k > 1 only) and the flags word. Its contents need
- * no initialisation and are overwritten by every call.
+ * The workspace holds the flags word, the per-slot running argmax words and,
+ * for top_k > 1, the per-row maximum bins of the projection (which bound the
+ * top-k scores and let the chain skip hopeless columns) and the
+ * per-workgroup top-k partial lists. Its contents need no initialisation and
+ * are overwritten by every call.
  */
 size_t dspark_workspace_bytes(int B, int L, int V, int top_k, int layout);
 
@@ -150,6 +152,24 @@ int dspark_propose(const void* hidden, int hidden_dtype, const uint16_t* lm_head
                    float* logits, void* workspace, size_t workspace_bytes, int32_t* tokens,
                    int32_t* candidates, float* cand_logits, float* conf, int32_t* lengths,
                    void* stream);
+
+/*
+ * dspark_propose with three HIP events (hipEvent_t, each may be NULL)
+ * recorded on `stream` between its launches: mark_init after the per-call
+ * set-up kernel, mark_projected after the lm_head projection, mark_chained
+ * after the last chain step (before the kernel that assembles candidates and
+ * confidences). The launches and results are those of dspark_propose; the
+ * events let a caller time each phase of the very launches a call makes. A
+ * failed event record returns DSPARK_ERR_HIP.
+ */
+int dspark_propose_marked(const void* hidden, int hidden_dtype, const uint16_t* lm_head,
+                          const float* lm_head_bias, const uint16_t* markov_w1,
+                          const uint16_t* markov_w2, const uint16_t* conf_w,
+                          const int32_t* anchors, int B, int L, int H, int V, int r, int layout,
+                          int top_k, float p_min, float* logits, void* workspace,
+                          size_t workspace_bytes, int32_t* tokens, int32_t* candidates,
+                          float* cand_logits, float* conf, int32_t* lengths, void* stream,
+                          void* mark_init, void* mark_projected, void* mark_chained);
 
 /*
  * Step 1 alone: the lm_head projection into `logits` (same arguments and

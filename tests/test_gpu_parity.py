@@ -181,6 +181,44 @@ def test_chain_alone_on_oracle_logits(dev, orc):
     assert dsp.read_flags(res) == 0
 
 
+BOUND_CASES = {
+    "throughput_like_B64_k4": lambda: make_small(64, 4, 128, 40000, 128, top_k=4, conf=True,
+                                                 p_min=0.3, w_std=0.05, seed=51),
+    "tree_like_B8_k4": lambda: make_small(8, 5, 128, 60000, 128, top_k=4, w_std=0.05, seed=52),
+    "k16_r64": lambda: make_small(12, 3, 64, 30000, 64, top_k=16, w_std=0.2, seed=53),
+    "k3_strong_markov": lambda: make_small(40, 4, 64, 20000, 32, top_k=3, w_std=0.5, seed=54),
+    "k2_rank256": lambda: make_small(6, 3, 128, 9000, 256, top_k=2, w_std=0.2, seed=55),
+    "k4_bias_ragged": lambda: make_small(37, 5, 320, 5003, 16, top_k=4, reachable=900, seed=56),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BOUND_CASES))
+def test_bound_changes_nothing(dev, orc, name):
+    """dspark_propose filters its top-k inserts with a bound taken from the
+    projection's row maxima; dspark_chain on the same projections runs
+    without it. The bound only drops columns that cannot be among the top
+    k, so every output must be identical, bit for bit, and the proposal
+    must pass the oracle check."""
+    import torch
+
+    import dspark_block_drafter_amd as dsp
+    from devutil import run_propose, to_device, to_host
+    inp = BOUND_CASES[name]()
+    c = inp.cfg
+    d = to_device(inp)
+    res = to_host(run_propose(inp, dev=d))
+    logits = torch.from_numpy(res["logits"]).to(dev)
+    plain = dsp.chain(logits, d["markov_w1"], d["markov_w2"], d["anchors"], B=c.B, L=c.L,
+                      layout=c.layout, top_k=c.top_k, p_min=c.p_min, hidden=d["hidden"],
+                      conf_w=d["conf_w"])
+    torch.cuda.synchronize()
+    assert dsp.read_flags(plain) == 0
+    plain = to_host(plain)
+    for k in ("tokens", "candidates", "cand_logits", "conf", "lengths"):
+        assert np.array_equal(res[k], plain[k]), k
+    check(orc, inp, res)
+
+
 def test_logits_alone(dev, orc):
     import torch
 
