@@ -61,19 +61,31 @@ __device__ __forceinline__ u64 make_key(float score, int id) {
 __device__ __forceinline__ int key_id(u64 key) { return (int)(~(uint32_t)key); }
 __device__ __forceinline__ float key_score(u64 key) { return unorder_f32((uint32_t)(key >> 32)); }
 
-// Largest value over the 32 lanes of this lane's half wave (lanes 0-31 or
-// 32-63), in every lane of the half: quad exchanges and row rotations (DPP),
-// then the other 16 lanes of the half (ds_swizzle, xor 16).
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, false));
+// Lane exchange within a half wave (ds_swizzle, bitmask mode): the value of
+// lane l ^ X, X < 32.
+template <int X>
+__device__ __forceinline__ float swz_xor(float v) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1F | (X << 10)));
 }
-__device__ __forceinline__ float half_wave_max(float v) {
-    v = fmaxf(v, dpp_f32<0xB1>(v));    // quad_perm [1,0,3,2]
-    v = fmaxf(v, dpp_f32<0x4E>(v));    // quad_perm [2,3,0,1]
-    v = fmaxf(v, dpp_f32<0x124>(v));   // row_ror:4
-    v = fmaxf(v, dpp_f32<0x128>(v));   // row_ror:8
-    return fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));
+
+// Row maxima of a 32 x 32 accumulator block over its 32 columns: lane l holds
+// v[g] for row acc_row(g, l) of column l % 32. A butterfly over the five lane
+// bits of the half wave: at the step on bit b every lane keeps the half of
+// its rows selected by its own bit b and folds in its partner's (lane ^ 2^b)
+// values of those rows, so 16 + 8 + 4 + 2 + 1 exchanges in all. Lane l ends
+// with the maximum of row acc_row((l >> 1) & 15, l) (lanes l and l ^ 1 hold
+// the same row).
+__device__ __forceinline__ float block_row_max(const float (&v)[16], int lane) {
+    const bool b4 = (lane >> 4) & 1, b3 = (lane >> 3) & 1, b2 = (lane >> 2) & 1, b1 = (lane >> 1) & 1;
+    float w8[8], w4[4], w2[2];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w8[k] = fmaxf(b4 ? v[k + 8] : v[k], swz_xor<16>(b4 ? v[k] : v[k + 8]));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w4[k] = fmaxf(b3 ? w8[k + 4] : w8[k], swz_xor<8>(b3 ? w8[k] : w8[k + 4]));
+#pragma unroll
+    for (int k = 0; k < 2; ++k) w2[k] = fmaxf(b2 ? w4[k + 2] : w4[k], swz_xor<4>(b2 ? w4[k] : w4[k + 2]));
+    const float w1 = fmaxf(b1 ? w2[1] : w2[0], swz_xor<2>(b1 ? w2[0] : w2[1]));
+    return fmaxf(w1, swz_xor<1>(w1));
 }
 
 __device__ __forceinline__ u64 shfl_xor_u64(u64 v, int mask) {

@@ -24,20 +24,22 @@ constexpr size_t kFlagsBytes = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t winners_off, bins_off, partials_off, total;
+    size_t winners_off, kth_off, smax_off, partials_off, total;
 };
 
-// [flags (256 B): flags word, gate's slot count, markov_w2 norm word]
+// [flags (256 B): flags word, gate's slot count, markov_w2 and markov_w1 norm words]
 // [winners: n_pred*kWinnerWays*winners_stride(B) u64]
-// [bins: B*n_pred*kBoundBins u32, top_k > 1]
+// [k-th slab maxima: B*n_pred f32]
+// [slab maxima: B*n_pred*ceil(V/kSlabCols) f32]
 // [partials: n_pred*B*nwg*top_k u64, top_k > 1]
 Layout workspace_layout(int B, int n_pred, int V, int top_k) {
     Layout l;
     l.winners_off = kFlagsBytes;
     const size_t win = align_up((size_t)n_pred * kWinnerWays * (size_t)winners_stride(B) * 8u);
-    l.bins_off = l.winners_off + win;
-    const size_t bins = top_k > 1 ? align_up((size_t)B * n_pred * kBoundBins * 4u) : 0;
-    l.partials_off = l.bins_off + bins;
+    l.kth_off = l.winners_off + win;
+    l.smax_off = l.kth_off + align_up((size_t)B * n_pred * 4u);
+    const size_t smax = align_up((size_t)B * n_pred * ((V + kSlabCols - 1) / kSlabCols) * 4u);
+    l.partials_off = l.smax_off + smax;
     const size_t part =
         top_k > 1 ? align_up((size_t)n_pred * B * (size_t)chain_workgroups_max(V) * top_k * 8u) : 0;
     l.total = l.partials_off + part;
@@ -45,10 +47,10 @@ Layout workspace_layout(int B, int n_pred, int V, int top_k) {
 }
 
 // Byte offsets of the words in the flags block.
-constexpr size_t kStopWord = 4, kW2NormWord = 8;
+constexpr size_t kStopWord = 4, kW2NormWord = 8, kW1NormWord = 12;
 // Extra workgroups of the projection that take the markov_w2 norm for the
 // top-k bound (they run in the projection's last, partly filled round).
-constexpr int kW2NormGroups = 64;
+constexpr int kW2NormGroups = 256;
 
 int first_pred(int layout) { return layout == DSPARK_LAYOUT_BONUS_ANCHOR ? 1 : 0; }
 
@@ -97,12 +99,13 @@ struct ChainExtras {
     const int32_t* top_k_b = nullptr; // adaptive: candidates kept per block
 };
 
-// Arguments of the chain kernels over V columns. With `bounded` (top_k > 1
-// only) the chain reads the top-k bound that the projection of the same
-// call leaves in the workspace.
+// Arguments of the chain kernels over V columns. With `bounded` the chain
+// reads the bound that the projection of the same call leaves in the
+// workspace (bins, slab maxima, row norms).
 ChainArgs chain_args(const float* logits, const uint16_t* w1, const uint16_t* w2,
-                     const ChainExtras& x, const int32_t* anchors, int B, int L, int V, int r,
-                     int layout, int top_k, void* workspace, int32_t* lengths, bool bounded) {
+                     const ChainExtras& x, const int32_t* anchors, int B, int L, int H, int V, int r,
+                     int layout, int top_k, bool hidden_f32, void* workspace, int32_t* lengths,
+                     bool bounded) {
     const int n_pred = L - first_pred(layout);
     const Layout wl = workspace_layout(B, n_pred, V, top_k);
     char* ws = static_cast<char*>(workspace);
@@ -123,11 +126,22 @@ ChainArgs chain_args(const float* logits, const uint16_t* w1, const uint16_t* w2
     c.r = r;
     c.n_pred = n_pred;
     c.top_k = top_k;
-    c.nwg = chain_workgroups(B, V, r, top_k);
+    // The projection leaves a bound when the chain can use it: the pruned
+    // form (one block group, pipelined vocabulary, rank up to 128) uses the
+    // slab maxima, their k-th largest per row and both norms; the other forms
+    // filter top-k inserts with the k-th largest and the markov_w2 norm.
+    bounded = bounded && top_k > 1;
+    const bool sparse = bounded && B <= 32 && chain_sparse(V, r);
+    c.nwg = sparse ? chain_sparse_workgroups(B, V, r, top_k) : chain_workgroups(B, V, r, top_k);
     c.wstride = winners_stride(B);
-    const bool bound = bounded && top_k > 1;
-    c.bins = bound ? reinterpret_cast<uint32_t*>(ws + wl.bins_off) : nullptr;
-    c.w2n2 = bound ? reinterpret_cast<uint32_t*>(ws + kW2NormWord) : nullptr;
+    c.kth = bounded ? reinterpret_cast<float*>(ws + wl.kth_off) : nullptr;
+    c.smax = bounded ? reinterpret_cast<const float*>(ws + wl.smax_off) : nullptr;
+    c.w2n2 = bounded ? reinterpret_cast<uint32_t*>(ws + kW2NormWord) : nullptr;
+    c.w1n2 = sparse ? reinterpret_cast<uint32_t*>(ws + kW1NormWord) : nullptr;
+    c.sparse = sparse ? 1 : 0;
+    // the pruned form reads slabs of kSlabCols; otherwise the four-wave
+    // projection takes one wave's columns per slab
+    c.slab_cols = !sparse && gemm_four_wave(B * n_pred, H, L, n_pred, hidden_f32) ? kSlabColsWide : kSlabCols;
     return c;
 }
 
@@ -162,6 +176,7 @@ int run_chain(const ChainArgs& c, bool initialised, const void* hidden, int hidd
         g.hidden_f32 = hidden_dtype == DSPARK_HIDDEN_F32;
         e = launch_gate(g, stream);
     }
+    if (e == hipSuccess && c.kth) e = launch_row_kth(c, stream);
     for (int j = 0; j < n_pred && e == hipSuccess; ++j) e = launch_chain_step(c, j, stream);
     if (e == hipSuccess && mark_chained) e = hipEventRecord(mark_chained, stream);
     if (e != hipSuccess) return DSPARK_ERR_HIP;
@@ -207,13 +222,17 @@ GemmArgs gemm_args(const void* hidden, const uint16_t* lm_head, const float* bia
     g.N = V;
     g.K = H;
     g.L = L;
-    if (c != nullptr && c->bins != nullptr) {
-        g.bins = c->bins;
+    if (c != nullptr && c->smax != nullptr) {
+        g.smax = const_cast<float*>(c->smax);
+        g.slab_cols = c->slab_cols;
         if (r > 0) {
             g.w2 = c->w2;
+            g.w1 = c->w1;
             g.w2_rows = V;
+            g.w1_rows = c->vocab;
             g.w2_rank = r;
             g.w2n2 = c->w2n2;
+            g.w1n2 = c->w1n2;   // (nullptr: markov_w2 only)
             g.w2_groups = kW2NormGroups;
         }
     }
@@ -256,8 +275,9 @@ int propose_impl(const void* hidden, int hidden_dtype, const uint16_t* lm_head,
     const int n_pred = L - first_pred(layout);
     if (workspace_bytes < workspace_layout(B, n_pred, V, top_k).total) return DSPARK_ERR_WORKSPACE;
 
-    const ChainArgs c = chain_args(logits, markov_w1, markov_w2, ChainExtras(), anchors, B, L, V, r,
-                                   layout, top_k, workspace, lengths, true);
+    const ChainArgs c = chain_args(logits, markov_w1, markov_w2, ChainExtras(), anchors, B, L, H, V, r,
+                                   layout, top_k, hidden_dtype == DSPARK_HIDDEN_F32, workspace, lengths,
+                                   true);
     st = project(c, hidden, hidden_dtype, lm_head, lm_head_bias, B, L, H, V, layout, logits, s,
                  mark_init, mark_projected);
     if (st != DSPARK_OK) return st;
@@ -310,8 +330,9 @@ int dspark_chain(const float* logits, const void* hidden, int hidden_dtype,
     if (workspace_bytes < dspark_workspace_bytes(B, L, V, top_k, layout)) return DSPARK_ERR_WORKSPACE;
     if (!aligned16(logits)) return DSPARK_ERR_UNSUPPORTED;
     // caller projections: no bound from a projection of this call
-    const ChainArgs c = chain_args(logits, markov_w1, markov_w2, ChainExtras(), anchors, B, L, V, r,
-                                   layout, top_k, workspace, lengths, false);
+    const ChainArgs c = chain_args(logits, markov_w1, markov_w2, ChainExtras(), anchors, B, L, H, V, r,
+                                   layout, top_k, hidden_dtype == DSPARK_HIDDEN_F32, workspace, lengths,
+                                   false);
     return run_chain(c, false, hidden, hidden_dtype, ChainExtras(), conf_w, B, L, H, V, layout, top_k,
                      p_min, workspace, tokens, candidates, cand_logits, conf, lengths,
                      static_cast<hipStream_t>(stream));
@@ -372,8 +393,8 @@ int dspark_propose_d2t(const void* hidden, int hidden_dtype, const uint16_t* lm_
     ChainExtras x;
     x.d2t = d2t;
     x.vocab = V;
-    const ChainArgs c = chain_args(logits, markov_w1, markov_w2, x, anchors, B, L, D, r, layout,
-                                   top_k, workspace, lengths, true);
+    const ChainArgs c = chain_args(logits, markov_w1, markov_w2, x, anchors, B, L, H, D, r, layout,
+                                   top_k, hidden_dtype == DSPARK_HIDDEN_F32, workspace, lengths, true);
     st = project(c, hidden, hidden_dtype, lm_head, nullptr, B, L, H, D, layout, logits, s);
     if (st != DSPARK_OK) return st;
     return run_chain(c, true, hidden, hidden_dtype, x, conf_w, B, L, H, D, layout, top_k, p_min,
@@ -405,8 +426,8 @@ int dspark_propose_adaptive(const void* hidden, int hidden_dtype, const uint16_t
     ChainExtras x;
     x.p_min_b = p_min;
     x.top_k_b = block_top_k;
-    const ChainArgs c = chain_args(logits, markov_w1, markov_w2, x, anchors, B, L, V, r, layout,
-                                   top_k, workspace, lengths, true);
+    const ChainArgs c = chain_args(logits, markov_w1, markov_w2, x, anchors, B, L, H, V, r, layout,
+                                   top_k, hidden_dtype == DSPARK_HIDDEN_F32, workspace, lengths, true);
     st = project(c, hidden, hidden_dtype, lm_head, lm_head_bias, B, L, H, V, layout, logits, s);
     if (st != DSPARK_OK) return st;
     return run_chain(c, true, hidden, hidden_dtype, x, conf_w, B, L, H, V, layout, top_k, 0.0f,

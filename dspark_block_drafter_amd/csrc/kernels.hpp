@@ -8,14 +8,23 @@
 namespace dspark {
 
 // ---- lm_head projection ---------------------------------------------------
-// Row-maximum bins: a lower bound on the top-k scores of every chain slot,
-// produced by the projection's epilogue. The columns of a row are cut into
-// slabs (the columns one wave of a tile holds); slab s raises bin
-// s % kBoundBins of row m to the largest projection of the row over the
-// slab's columns (as an order_f32 key; 0 = no column yet). The bins partition
-// the columns, so every non-empty bin is the projection of a distinct column:
-// the k-th largest bin is at most the k-th largest projection of the row.
-constexpr int kBoundBins = 16;
+// Slab maxima: with them, the projection's epilogue also writes, for every
+// row m and every slab of slab_cols columns, the largest projection of the
+// row over the slab: smax[m][s], layout [M][ceil(N / slab_cols)]. A pass
+// after the projection takes each row's k-th largest slab maximum (a lower
+// bound on the row's k-th largest projection: the slabs are disjoint), and
+// the chain bounds its top-k scores with it; the pruned chain form also
+// skips slabs of kSlabCols columns in which no column can reach a block's
+// top k. The four-wave projection kernel takes slabs of kSlabColsWide (one
+// wave's columns) when the pruned form does not run: half the epilogue work.
+constexpr int kSlabCols = 64;
+constexpr int kSlabColsWide = 128;
+// Whether launch_lmhead_gemm runs the four-wave kernel for these sizes
+// (bf16 hidden, K % 64 == 0, M > 128, 32-bit buffer offsets).
+inline bool gemm_four_wave(int M, int K, int L, int n_pred, bool hidden_f32) {
+    const long hid_bytes = (long)((M + n_pred - 1) / n_pred) * L * K * 2;
+    return !hidden_f32 && K % 64 == 0 && M > 128 && hid_bytes < 0xFFFFFFFFL && 256L * K * 2 < 0x7FFFFFFFL;
+}
 
 struct GemmArgs {
     const void* hidden;      // [B, L, H] bf16 bits or fp32
@@ -24,13 +33,17 @@ struct GemmArgs {
     float* out;              // [M, V], M = B * n_pred
     int M, N, K;             // M rows, N = V, K = H
     int L, n_pred, i_first;  // row m reads hidden row (m / n_pred) * L + i_first + m % n_pred
-    uint32_t* bins;          // [M, kBoundBins] row-maximum bins (zeroed before), or nullptr
-    // With bins: the largest squared row norm of markov_w2 [w2_rows, w2_rank]
-    // is raised into *w2n2 (fp32 bits, zeroed before) by w2_groups extra
-    // workgroups after the tiles of the launch (they run in its last round).
+    float* smax;             // slab maxima [M][ceil(N / slab_cols)], or nullptr
+    int slab_cols;           // kSlabCols, or kSlabColsWide for the four-wave kernel
+    // With w2n2: the largest squared row norms of markov_w2 [w2_rows, w2_rank]
+    // and markov_w1 [w1_rows, w2_rank] are raised into *w2n2 and *w1n2 (fp32
+    // bits, zeroed before) by w2_groups extra workgroups after the tiles of
+    // the launch (they run in its last, partly filled round).
     const uint16_t* w2;
-    int w2_rows, w2_rank, w2_groups;
+    const uint16_t* w1;
+    int w2_rows, w1_rows, w2_rank, w2_groups;
     uint32_t* w2n2;
+    uint32_t* w1n2;
 };
 hipError_t launch_lmhead_gemm(const GemmArgs& a, bool hidden_f32, hipStream_t stream);
 
@@ -94,6 +107,24 @@ inline int chain_workgroups(int B, int V, int r, int top_k) {
                     : f == kChainWave ? kChainCUs * chain_wave_per_cu(B, r, top_k) : kChainCUs;
     return nt < cap ? nt : cap;
 }
+// Pruned form (chain_step_sparse: a propose call whose projection left the
+// slab maxima; V % 4 == 0, rank up to 128): per-wave rings like kChainWave,
+// with LDS budgets that leave room for the skip lists; at least one slab per
+// wave where the vocabulary allows.
+constexpr int kChainSparseBudget2 = 72 * 1024;   // per workgroup, two per CU
+constexpr int kChainSparseBudget1 = 150 * 1024;  // one per CU
+inline bool chain_sparse(int V, int r) { return chain_pipelined(V) && (r + 15) / 16 <= 8; }
+inline int chain_sparse_per_cu(int B, int r, int top_k) {
+    const int rows = chain_wave_rows(B, top_k);
+    return rows < 32 && 4 * 2 * chain_wave_stage_bytes(chain_wave_rank(r), rows) <= kChainSparseBudget2 ? 2 : 1;
+}
+inline int chain_sparse_workgroups(int B, int V, int r, int top_k) {
+    const int vw = B > 32 ? 2 : 4;   // waves per block group
+    const int slabs = (V + kSlabCols - 1) / kSlabCols;
+    const int want = (slabs + vw - 1) / vw;
+    const int cap = kChainCUs * chain_sparse_per_cu(B, r, top_k);
+    return want < cap ? want : cap;
+}
 // Upper bound of chain_workgroups over every rank (workspace sizing does not
 // know r): the narrowest tile gives the most workgroups.
 inline int chain_workgroups_max(int V) {
@@ -134,13 +165,23 @@ struct ChainArgs {
     int wstride;               // winners_stride(B)
     int vocab;                 // target vocabulary size (== V without d2t)
     const int32_t* stop;       // adaptive gate: slots from *stop on are skipped (nullptr: none)
-    // Top-k bound (top_k > 1, after a projection that filled them), or nullptr:
-    // bins [B * n_pred, kBoundBins] (GemmArgs) and the largest squared row
-    // norm of markov_w2 (fp32 bits).
-    uint32_t* bins;
+    // Bound (after a projection of the same call), or nullptr: slab maxima
+    // [B * n_pred][ceil(V / slab_cols)] (GemmArgs), the k-th largest slab
+    // maximum of every row [B * n_pred] (row_kth, k = the list length), and
+    // the largest squared row norms of markov_w2 and markov_w1 (fp32 bits;
+    // markov_w1 only for the pruned form).
+    const float* smax;
+    float* kth;
     uint32_t* w2n2;
+    uint32_t* w1n2;
+    int slab_cols;
+    // The pruned form runs the steps (chain_step_sparse): set only with smax,
+    // kth, w2n2 and w1n2 all present (and chain_sparse(V, r)).
+    int sparse;
 };
-// Zeroes the running-argmax words, the flags, the bins and *w2n2 (when
+// The k-th largest slab maximum of every row (after the projection).
+hipError_t launch_row_kth(const ChainArgs& a, hipStream_t stream);
+// Zeroes the running-argmax words, the flags and the norm words (when
 // present) and presets lengths to n_pred; enqueued before the projection.
 hipError_t launch_chain_init(const ChainArgs& a, hipStream_t stream);
 hipError_t launch_chain_step(const ChainArgs& a, int j, hipStream_t stream);

@@ -31,59 +31,133 @@ constexpr int BK = 64;
 // non-temporal: the logits are streamed out once and should not evict the
 // lm_head / hidden tiles from L2. The bias is read once per column before any
 // store, and tiles that lie wholly inside the matrix store without predicates.
-// An extra workgroup g (of a.w2_groups, numbered after the tiles) of a
-// projection launch: the largest squared row norm of markov_w2 over rows
-// g * T + t, (g + G) * T + t, ... (T threads), a sum of squares of bf16 values
-// in fp32 (every square is exact), raised into *w2n2 as fp32 bits (the bits
-// of non-negative floats order as unsigned integers).
-__device__ __forceinline__ void w2_norm_part(const GemmArgs& a, int g) {
-    const int nt = blockDim.x, tid = threadIdx.x, r = a.w2_rank;
+// Largest squared row norm of a bf16 matrix [rows, r], r a multiple of 8,
+// taken by G workgroups (this is group g): a sum of squares of bf16 values in
+// fp32 (every square is exact), raised into *out as fp32 bits (the bits of
+// non-negative floats order as unsigned integers). When a row is a power of
+// two of 16-byte chunks (r = 8, 16, ..., 256) the wave reads the matrix as
+// consecutive 16-byte chunks, 16 per lane in flight, and sums each row over
+// the aligned group of lanes that hold its chunks; otherwise each thread sums
+// whole rows.
+__device__ __forceinline__ void row_norm_part(const uint16_t* w, long rows, int r, int g, int G,
+                                              uint32_t* out) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int nw = blockDim.x >> 6, wave = tid >> 6;
+    const int cpr = r >> 3;   // 16-byte chunks per row
     float best = 0.0f;
-    for (long row = (long)g * nt + tid; row < a.w2_rows; row += (long)a.w2_groups * nt) {
-        const uint16_t* p = a.w2 + row * r;
-        float s = 0.0f;
-        for (int k = 0; k < r; k += 8) {
-            const u32x4 w = *reinterpret_cast<const u32x4*>(p + k);
+    if ((cpr & (cpr - 1)) == 0 && cpr <= 64) {
+        constexpr int U = 16;
+        const long chunks = rows * cpr;
+        const u32x4* p = reinterpret_cast<const u32x4*>(w);
+        // wave-steps of 64 U chunks; wave (g, wave) takes steps g * nw + wave + k * G * nw
+        for (long base = ((long)g * nw + wave) * 64 * U; base < chunks; base += (long)G * nw * 64 * U) {
+            u32x4 x[U];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float lo = bf16_lo(w[q]), hi = bf16_hi(w[q]);
-                s += lo * lo;
-                s += hi * hi;
+            for (int u = 0; u < U; ++u) {
+                const long c = base + u * 64 + lane;
+                x[u] = c < chunks ? p[c] : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float s = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float lo = bf16_lo(x[u][q]), hi = bf16_hi(x[u][q]);
+                    s += lo * lo;
+                    s += hi * hi;
+                }
+                // the row's sum over its cpr lanes (aligned groups of the 64)
+                for (int m = 1; m < cpr; m <<= 1) s += __shfl_xor(s, m, kWave);
+                best = fmaxf(best, s);
             }
         }
-        best = fmaxf(best, s);
+    } else {
+        const int nt = blockDim.x;
+        for (long row = (long)g * nt + tid; row < rows; row += (long)G * nt) {
+            const uint16_t* q0 = w + row * r;
+            float s = 0.0f;
+            for (int k = 0; k < r; k += 8) {
+                const u32x4 x = *reinterpret_cast<const u32x4*>(q0 + k);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float lo = bf16_lo(x[q]), hi = bf16_hi(x[q]);
+                    s += lo * lo;
+                    s += hi * hi;
+                }
+            }
+            best = fmaxf(best, s);
+        }
     }
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) best = fmaxf(best, __shfl_xor(best, m, kWave));
-    if ((tid & 63) == 0) atomicMax(a.w2n2, __float_as_uint(best));
+    if (lane == 0) atomicMax(out, __float_as_uint(best));
 }
 
-// Row-maximum bins (kernels.hpp, kBoundBins) of a wave's FM x FN block in
-// the plain accumulator layout: the lane holds column nb + 32 j + lane % 32
-// and, in register g, row mb + 32 i + acc_row(g, lane). The wave's columns
-// form one slab. Per row: the largest projection over the lane's columns,
-// then over the 32 lanes of the half wave; lane g of each half raises the
-// bin of the half's row g.
-template <int FM, int FN>
-__device__ __forceinline__ void row_bins(const GemmArgs& a, const f32x16 (&acc)[FM][FN],
-                                         const float (&bn)[FN], int mb, int nb, int slab_cols, int lane) {
-    if (nb >= a.N) return;   // no column of this wave's slab exists
-    const int lrow = lane & 31;
-    uint32_t* bin = a.bins + (nb / slab_cols) % kBoundBins;
+// An extra workgroup g (of a.w2_groups, numbered after the tiles) of a
+// projection launch: its share of the markov_w2 and (when wanted) markov_w1
+// row norms.
+__device__ __forceinline__ void w2_norm_part(const GemmArgs& a, int g) {
+    row_norm_part(a.w2, a.w2_rows, a.w2_rank, g, a.w2_groups, a.w2n2);
+    if (a.w1n2 != nullptr) row_norm_part(a.w1, a.w1_rows, a.w2_rank, g, a.w2_groups, a.w1n2);
+}
+
+// Slab maxima (kernels.hpp) of SC columns of a wave's FM x FN block in the
+// plain accumulator layout: the lane holds column nb + 32 j + lane % 32 and,
+// in register g, row mb + 32 i + acc_row(g, lane). Per row and slab: the
+// largest projection over the lane's columns of the slab, then over the 32
+// lanes of the half wave (block_row_max), stored by the even lanes. A wave of
+// 32 columns (FN == 1) holds half a 64-column slab: waves 2t and 2t + 1 (the
+// same rows, neighbouring columns) combine their halves through LDS.
+template <int FM, int FN, int NW, int SC>
+__device__ __forceinline__ void slab_maxima(const GemmArgs& a, const f32x16 (&acc)[FM][FN],
+                                            const float (&bn)[FN], int mb, int nb, int wave, int lane) {
+    static_assert((FN == 1 && SC == 64) || FN % (SC / 32) == 0, "a wave holds half a slab or whole slabs");
+    constexpr int JS = FN == 1 ? 1 : SC / 32;  // 32-column blocks per slab in the wave
+    constexpr int SW = FN / JS;                // slabs (or half slabs) per wave
+    const int lrow = lane & 31, N = a.N;
+    const int nslab = (N + SC - 1) / SC;
+    const int row = acc_row((lane >> 1) & 15, lane);   // the row this lane ends with
+    float pick[FM][SW];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int q = 0; q < SW; ++q) {
+            float v[16];
+#pragma unroll
+            for (int g = 0; g < 16; ++g) {
+                v[g] = -INFINITY;
+#pragma unroll
+                for (int jj = 0; jj < JS; ++jj) {
+                    const int j = q * JS + jj;
+                    if (nb + j * 32 + lrow < N) v[g] = fmaxf(v[g], acc[i][j][g] + bn[j]);
+                }
+            }
+            pick[i][q] = block_row_max(v, lane);
+        }
+    if constexpr (FN == 1) {
+        static_assert(NW % 2 == 0, "waves pair up");
+        __shared__ float s_half[NW][FM * 32];
+        if ((lane & 1) == 0) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) s_half[wave][i * 32 + row] = pick[i][0];
+        }
+        __syncthreads();
+        if ((lane & 1) == 0) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) pick[i][0] = fmaxf(pick[i][0], s_half[wave ^ 1][i * 32 + row]);
+        }
+        if (wave & 1) return;   // the even wave of the pair writes the slab
+    }
+    if (lane & 1) return;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-        float pick = -INFINITY;
+        const int m = mb + i * 32 + row;
+        if (m >= a.M) continue;
 #pragma unroll
-        for (int g = 0; g < 16; ++g) {
-            float v = -INFINITY;
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                if (nb + j * 32 + lrow < a.N) v = fmaxf(v, acc[i][j][g] + bn[j]);
-            v = half_wave_max(v);
-            pick = lrow == g ? v : pick;
+        for (int q = 0; q < SW; ++q) {
+            const int n = nb + q * SC;
+            if (n < N) a.smax[(long)m * nslab + n / SC] = pick[i][q];
         }
-        const int m = mb + i * 32 + acc_row(lrow, lane);
-        if (lrow < 16 && m < a.M) atomicMax(bin + (long)m * kBoundBins, order_f32(pick));
     }
 }
 
@@ -102,7 +176,21 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x16 (&acc
     // The bias loads must be complete before the first store: otherwise the
     // wait inserted for them also waits for every store issued so far.
     __builtin_amdgcn_s_waitcnt(0);
-    if (a.bins != nullptr) row_bins<FM, FN>(a, acc, bn, m0 + wm * TM, n0 + wn * TN, TN, lane);
+    // (the layout puts waves wm * WN + wn and its neighbour wn ^ 1 on the same rows)
+    if (a.smax != nullptr) {
+        if constexpr (FN % (kSlabColsWide / 32) == 0) {
+            if (a.slab_cols == kSlabColsWide) {
+                slab_maxima<FM, FN, WM * WN, kSlabColsWide>(a, acc, bn, m0 + wm * TM, n0 + wn * TN,
+                                                             wm * WN + wn, lane);
+            } else {
+                slab_maxima<FM, FN, WM * WN, kSlabCols>(a, acc, bn, m0 + wm * TM, n0 + wn * TN,
+                                                        wm * WN + wn, lane);
+            }
+        } else {
+            slab_maxima<FM, FN, WM * WN, kSlabCols>(a, acc, bn, m0 + wm * TM, n0 + wn * TN,
+                                                    wm * WN + wn, lane);
+        }
+    }
     if (m0 + BM <= M && n0 + BN <= N) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
@@ -634,8 +722,7 @@ hipError_t launch_lmhead_gemm(const GemmArgs& a, bool hidden_f32, hipStream_t st
     if (!hidden_f32 && a.K % 32 == 0) {
         // buffer offsets are 32-bit: the hidden rows and one lm_head tile
         // must each span less than 4 GiB
-        const long hid_bytes = (long)((a.M + a.n_pred - 1) / a.n_pred) * a.L * a.K * 2;
-        if (a.M > 128 && a.K % 64 == 0 && hid_bytes < 0xFFFFFFFFL && 256L * a.K * 2 < 0x7FFFFFFFL) {
+        if (gemm_four_wave(a.M, a.K, a.L, a.n_pred, false)) {
             const long tiles = launch_groups(a, 256, 256);
             if (tiles > 0x7fffffffL) return hipErrorInvalidValue;
             hipLaunchKernelGGL(lmhead_gemm_w4, dim3((unsigned)tiles), dim3(256), 0, stream, a);

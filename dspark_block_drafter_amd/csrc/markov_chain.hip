@@ -36,14 +36,14 @@ static_assert(kChainTileV == kWaves * 32, "one 32-column block per wave");
 
 __global__ __launch_bounds__(256) void chain_init(u64* winners, int n, uint32_t* flags,
                                                   int32_t* lengths, int B, int n_pred,
-                                                  uint32_t* bins, int nbins, uint32_t* w2n2) {
+                                                  uint32_t* w2n2, uint32_t* w1n2) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) winners[i] = 0ull;
     if (i < B) lengths[i] = n_pred;
-    if (i < nbins) bins[i] = 0u;
     if (i == 0) {
         *flags = 0u;
         if (w2n2) *w2n2 = 0u;
+        if (w1n2) *w1n2 = 0u;
     }
 }
 
@@ -161,32 +161,71 @@ __device__ __forceinline__ void publish(const ChainArgs& a, int j, int bbase, u6
 
 // ---- top-k bound from the projection's row-maximum bins ----------------------
 
+// Insert x into the decreasing list top[0..KL).
+template <int KL>
+__device__ __forceinline__ void top_insert_f32(float (&top)[KL], float x) {
+#pragma unroll
+    for (int i = 0; i < KL; ++i) {
+        const float hi = fmaxf(x, top[i]);
+        x = fminf(x, top[i]);
+        top[i] = hi;
+    }
+}
+
+// The k-th largest slab maximum of every row: one workgroup per row; each
+// thread keeps the KL largest of its share of the slabs (up to 16 loads in
+// flight), then the lists are merged across the wave and the four waves.
+// -inf when the row has fewer than KL slabs.
+template <int KL>
+__global__ __launch_bounds__(256) void row_kth(const float* smax, int nslab, float* kth) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const float* row = smax + (long)blockIdx.x * nslab;
+    float top[KL];
+#pragma unroll
+    for (int i = 0; i < KL; ++i) top[i] = -INFINITY;
+    for (int s0 = 0; s0 < nslab; s0 += 256 * 16) {
+        float x[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int s = s0 + u * 256 + tid;
+            x[u] = s < nslab ? row[s] : -INFINITY;
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) top_insert_f32<KL>(top, x[u]);
+    }
+#pragma unroll
+    for (int mask = 1; mask < 64; mask <<= 1) {
+        float other[KL];
+#pragma unroll
+        for (int i = 0; i < KL; ++i) other[i] = __shfl_xor(top[i], mask, kWave);
+#pragma unroll
+        for (int i = 0; i < KL; ++i) top_insert_f32<KL>(top, other[i]);
+    }
+    __shared__ float s_top[kWaves][KL];
+    if (lane == 0) {
+#pragma unroll
+        for (int i = 0; i < KL; ++i) s_top[wave][i] = top[i];
+    }
+    __syncthreads();
+    if (tid == 0) {
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w)
+#pragma unroll
+            for (int i = 0; i < KL; ++i) top_insert_f32<KL>(top, s_top[w][i]);
+        kth[blockIdx.x] = top[KL - 1];
+    }
+}
+
 // Lower bound on the KL-th best biased score of one slot of one block, from
-// which its top-k filter starts. The KL largest row-maximum bins are the
-// projections of KL distinct columns of the row (kernels.hpp, kBoundBins);
-// the Markov term of any column is at most |markov_w2[v]| |u| in magnitude
+// which its top-k filter starts. The row's KL largest slab maxima are the
+// projections of KL distinct columns (the slabs are disjoint), and the
+// Markov term of any column is at most |markov_w2[v]| |u| in magnitude
 // (Cauchy-Schwarz, u = markov_w1[prev]), so those KL columns score at least
 // kth - |w2|max |u|. The scores are fp32 sums of r + 1 terms, within
 // (r + 1) 2^-24 (|z| + |bias|) of exact (r <= 256: below 2e-5 relative), and
-// the norms carry a few ulps: the margins below cover both. -inf when fewer
-// than KL bins are set (a row with fewer slabs than KL).
-template <int KL>
-__device__ __forceinline__ float chain_bound(const uint32_t (&kb)[kBoundBins], float w2n2, float un2) {
-    uint32_t top[KL];
-#pragma unroll
-    for (int i = 0; i < KL; ++i) top[i] = 0u;
-#pragma unroll
-    for (int t = 0; t < kBoundBins; ++t) {
-        uint32_t x = kb[t];
-#pragma unroll
-        for (int i = 0; i < KL; ++i) {   // insertion into the decreasing list
-            const uint32_t hi = x > top[i] ? x : top[i];
-            x = x > top[i] ? top[i] : x;
-            top[i] = hi;
-        }
-    }
-    if (top[KL - 1] == 0u) return -INFINITY;
-    const float kth = unorder_f32(top[KL - 1]);
+// the norms carry a few ulps: the margins below cover both. -inf without a
+// k-th slab.
+__device__ __forceinline__ float chain_bound(float kth, float w2n2, float un2) {
     const float mk = sqrtf(w2n2) * sqrtf(un2);
     return kth - mk * 1.001f - 1e-4f * (1.0f + fabsf(kth));
 }
@@ -207,22 +246,20 @@ __device__ __forceinline__ float w1_norm2(const u32x4 (&u)[RS > 0 ? RS : 1]) {
     return s + __shfl_xor(s, 32, kWave);
 }
 
-// Direct-to-LDS copy of the bins of slot j of blocks bbase .. bbase + NBL - 1
-// (rows past B repeat block B - 1) into s_bins[NBL][kBoundBins], and of the
-// markov_w2 norm word into all 64 words of s_w2n2; issued by the first
-// NBL / 16 waves (64 lanes x 16 bytes each) and the last wave.
-template <int NBL>
-__device__ __forceinline__ void load_bound(const ChainArgs& a, int j, int bbase, uint32_t (*s_bins)[kBoundBins],
-                                           uint32_t* s_w2n2, int wave, int lane) {
-    static_assert(NBL % 16 == 0 && NBL / 16 <= kWaves, "one 16-byte copy per lane");
-    if (wave < NBL / 16) {
-        const int c = wave * 64 + lane, blk = c >> 2, part = c & 3;
-        const int b = min(bbase + blk, a.B - 1);
-        const uint32_t* src = a.bins + ((long)b * a.n_pred + j) * kBoundBins + part * 4;
-        __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)&s_bins[wave * 16][0], 16, 0, 0);
+// Direct-to-LDS copy, by wave 0, of the k-th slab maxima of slot j of blocks
+// bbase + lane into s_kth[64] (blocks past B repeat block B - 1), and, by the
+// last wave, of the markov_w2 (and, with s_w1n2, markov_w1) norm word into
+// all 64 words of s_w2n2 (s_w1n2).
+__device__ __forceinline__ void load_bound(const ChainArgs& a, int j, int bbase, float* s_kth,
+                                           uint32_t* s_w2n2, int wave, int lane, uint32_t* s_w1n2 = nullptr) {
+    if (wave == 0) {
+        const int b = min(bbase + lane, a.B - 1);
+        __builtin_amdgcn_global_load_lds((const void*)(a.kth + (long)b * a.n_pred + j), (lds_ptr)s_kth, 4, 0, 0);
     }
-    if (wave == kWaves - 1)
+    if (wave == kWaves - 1) {
         __builtin_amdgcn_global_load_lds((const void*)a.w2n2, (lds_ptr)s_w2n2, 4, 0, 0);
+        if (s_w1n2 && a.w1n2) __builtin_amdgcn_global_load_lds((const void*)a.w1n2, (lds_ptr)s_w1n2, 4, 0, 0);
+    }
 }
 
 // ---- step kernel for V % 4 == 0: operands staged through LDS -----------------
@@ -267,9 +304,9 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
     // block's KL-th best score in this workgroup, shared with the waves that
     // score the other columns of the same blocks.
     __shared__ float s_thr[kWaves][32];
-    // Row-maximum bins of the slot's blocks and the markov_w2 norm word (the
-    // top-k bound), copied in by the prologue.
-    __shared__ uint32_t s_bins[KL > 1 ? NB * 32 : 1][kBoundBins];
+    // The slot's k-th slab maxima of its blocks and the markov_w2 norm word
+    // (the top-k bound), copied in by the prologue.
+    __shared__ float s_kth[64];
     __shared__ uint32_t s_w2n2[64];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -279,9 +316,9 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
     if (a.stop && j >= *a.stop) return;
     const int bbase = blockIdx.y * NB * 32;
     // the bound's copies go first: the prologue's waits cover them
-    const bool bounded = KL > 1 && a.bins != nullptr;
+    const bool bounded = KL > 1 && a.kth != nullptr;
     if constexpr (KL > 1)
-        if (bounded) load_bound<NB * 32>(a, j, bbase, s_bins, s_w2n2, wave, lane);
+        if (bounded) load_bound(a, j, bbase, s_kth, s_w2n2, wave, lane);
     const int B = a.B, V = a.V, r = a.r;
     const int nT = (V + TS - 1) / TS, G = gridDim.x, g = blockIdx.x;
     const int t0 = (int)((long)nT * g / G), t1 = (int)((long)nT * (g + 1) / G);
@@ -544,10 +581,7 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
         if constexpr (KL > 1) {
             if (bounded) {
                 const float un2 = w1_norm2<RS>(u);
-                uint32_t kb[kBoundBins];
-#pragma unroll
-                for (int t = 0; t < kBoundBins; ++t) kb[t] = s_bins[nbw * 32 + lrow][t];
-                tau = chain_bound<KL>(kb, __uint_as_float(s_w2n2[0]), un2);
+                tau = chain_bound(s_kth[nbw * 32 + lrow], __uint_as_float(s_w2n2[0]), un2);
             }
         }
         score(0, S0);
@@ -650,9 +684,9 @@ __global__ __launch_bounds__(256) void chain_step_wave(ChainArgs a, int j) {
     __shared__ u32x4 ring[kWaves][NS][STAGE];
     // Top-k bound of each wave's lane pairs, per block (see consume below).
     __shared__ float s_thr[kWaves][32];
-    // Row-maximum bins of the slot's blocks and the markov_w2 norm word (the
-    // top-k bound).
-    __shared__ uint32_t s_bins[KL > 1 ? NB * 32 : 1][kBoundBins];
+    // The slot's k-th slab maxima of its blocks and the markov_w2 norm word
+    // (the top-k bound).
+    __shared__ float s_kth[64];
     __shared__ uint32_t s_w2n2[64];
 
     const int lane = threadIdx.x & 63;
@@ -661,9 +695,9 @@ __global__ __launch_bounds__(256) void chain_step_wave(ChainArgs a, int j) {
     const int vb = wave % VW, nbw = wave / VW;
     if (a.stop && j >= *a.stop) return;   // adaptive gate: every block was cut
     const int bbase = blockIdx.y * NB * 32;
-    const bool bounded = KL > 1 && a.bins != nullptr;
+    const bool bounded = KL > 1 && a.kth != nullptr;
     if constexpr (KL > 1)
-        if (bounded) load_bound<NB * 32>(a, j, bbase, s_bins, s_w2n2, wave, lane);
+        if (bounded) load_bound(a, j, bbase, s_kth, s_w2n2, wave, lane);
     const int B = a.B, V = a.V, r = a.r;
     const int nT = (V + TS - 1) / TS, G = gridDim.x, g = blockIdx.x;
     const int t0 = (int)((long)nT * g / G), t1 = (int)((long)nT * (g + 1) / G);
@@ -762,10 +796,7 @@ __global__ __launch_bounds__(256) void chain_step_wave(ChainArgs a, int j) {
     if constexpr (KL > 1) {
         if (bounded) {
             const float un2 = w1_norm2<RS>(u);
-            uint32_t kb[kBoundBins];
-#pragma unroll
-            for (int t = 0; t < kBoundBins; ++t) kb[t] = s_bins[nbw * 32 + lrow][t];
-            tau = chain_bound<KL>(kb, __uint_as_float(s_w2n2[0]), un2);
+            tau = chain_bound(s_kth[nbw * 32 + lrow], __uint_as_float(s_w2n2[0]), un2);
         }
     }
     asm volatile("" ::: "memory");
@@ -941,6 +972,379 @@ __global__ __launch_bounds__(256) void chain_step_wave(ChainArgs a, int j) {
 #pragma unroll
             for (int i = 0; i < KL; ++i) topk_insert<KL>(list, o[lrow * KL + i]);
         }
+        if (a.top_k > 1) {
+            u64* p = a.partials + (((long)j * B + bme) * a.nwg + g) * a.top_k;
+#pragma unroll
+            for (int i = 0; i < KL; ++i)
+                if (i < a.top_k) p[i] = list[i];
+        }
+        if (list[0] != 0ull) atomicMax(winner_word(a.winners, a.wstride, j, g, bme), list[0]);
+    }
+}
+
+// ---- pruned step kernel (after a projection that left slab maxima) ---------
+
+// The step of a proposal whose projection left the slab maxima and the bins
+// (kernels.hpp): per-wave rings as in chain_step_wave, but a wave streams only
+// the kSlabCols-column slabs in which some block of its group can still reach
+// its top k, and of those only the logits rows of such blocks.
+//
+// Skip rule. Let Bg = max_v |markov_w2[v]| max_p |markov_w1[p]| bound the
+// Markov term of any column under any previous token (Cauchy-Schwarz). The
+// KL columns behind the block's KL largest bins score at least kth - Bg, so
+// its KL-th best score is at least that; a column c of slab s scores at most
+// smax[s] + Bg. Slab s can therefore hold none of the block's top KL when
+// smax[s] < kth - 2 Bg (less margins for the fp32 rounding of the scores and
+// of the norms). Neither side depends on the previous token, so the skip
+// masks are known before the Markov row is gathered. Inside a streamed slab
+// the per-block filter of chain_step_wave applies, from the tighter bound
+// with the block's own |markov_w1[prev]|.
+//
+// Work split: wave w of the G * VW waves of a block group owns a contiguous
+// run of slabs; it examines them in passes of up to 64 (one per lane), and a
+// pass streams the compacted list of the slabs some block needs, two 32-column
+// steps each. A skipped block's logits rows are not read: its copies read one
+// fixed 16-byte chunk instead (the slab maxima's first, hot in the caches),
+// and its scores in that slab are ignored. No workgroup barrier inside the
+// loop; the workgroup merges and publishes once per slot as chain_step_wave.
+template <int NB, int KL, int RS, int NS, int LROWS>
+__global__ __launch_bounds__(256) void chain_step_sparse(ChainArgs a, int j) {
+    constexpr int VW = kWaves / NB;         // waves per block group
+    constexpr int WR = 2 * RS;              // 16-byte chunks per staged markov_w2 row
+    constexpr int WRd = WR > 0 ? WR : 1;
+    constexpr int LR = 8;                   // 16-byte chunks per staged logits row (32 columns)
+    constexpr int W_SLOTS = 32 * WR;
+    constexpr int L_SLOTS = LROWS * LR;
+    constexpr int STAGE = W_SLOTS + L_SLOTS;
+    constexpr int W_INST = W_SLOTS / 64, L_INST = L_SLOTS / 64;
+    constexpr int LW = W_INST + L_INST;     // copies per step per wave
+    static_assert(NB == 1 || NB == 2, "one or two block groups");
+    static_assert(NS >= 2 && NS * LW + RS < 64, "vmcnt range");
+    static_assert(LROWS == 8 || LROWS == 16 || LROWS == 32, "staged logits rows");
+    static_assert(RS * 64 <= STAGE, "W1 rows fit one stage");
+    static_assert(KL * 32 * 8 <= NS * STAGE * 16, "list merge reuses a wave's ring");
+    static_assert(kSlabCols == 64, "two 32-column steps per slab");
+    __shared__ u32x4 ring[kWaves][NS][STAGE];
+    __shared__ float s_thr[kWaves][32];            // top-k bounds shared by the waves of a group
+    __shared__ float s_kth[64];                    // the blocks' k-th slab maxima
+    __shared__ uint32_t s_w2n2[64], s_w1n2[64];    // the norm words (every word the same)
+    __shared__ float s_skip[kWaves][32];           // per wave: skip threshold of each block
+    __shared__ int s_slab[kWaves][64];             // per wave: the pass's needed slabs
+    __shared__ uint32_t s_need[kWaves][64];        // and their block masks
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int lrow = lane & 31, lhalf = lane >> 5;
+    const int vb = wave % VW, nbw = wave / VW;
+    if (a.stop && j >= *a.stop) return;   // adaptive gate: every block was cut
+    const int bbase = blockIdx.y * NB * 32;
+    load_bound(a, j, bbase, s_kth, s_w2n2, wave, lane, s_w1n2);
+    const int B = a.B, V = a.V, r = a.r;
+    const int nS = (V + kSlabCols - 1) / kSlabCols;
+    const long GW = (long)gridDim.x * VW, wg = (long)blockIdx.x * VW + vb;
+    const int gbase = bbase + nbw * 32;      // first block of this wave's group
+    // the wave's slabs (none for a group past the last block)
+    const int sb0 = (int)(nS * wg / GW), sb1 = gbase < B ? (int)(nS * (wg + 1) / GW) : sb0;
+    const int bme = gbase + lrow;
+    const bool active = bme < B;
+    // blocks of the group that exist, as a mask over the group's 32 blocks
+    const uint32_t exist = B - gbase >= 32 ? 0xFFFFFFFFu : (B > gbase ? (1u << (B - gbase)) - 1u : 0u);
+    // slab maxima of the first pass (register loads issued before the wait
+    // below, so they travel with the previous tokens): lane k reads slab
+    // pb + k of each of the group's blocks (rows b * n_pred + j)
+    float sm[32];
+    auto load_smax = [&](int pb) __attribute__((always_inline)) {
+        const int sl = min(pb + lane, sb1 - 1);   // (sb1 > pb whenever it is called)
+        const float* col = a.smax + ((long)gbase * a.n_pred + j) * nS + sl;
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+            // rows of blocks past B are not read (their row is clamped, the value dropped)
+            const float x = col[(long)min(k, B - 1 - gbase) * a.n_pred * nS];
+            sm[k] = gbase + k < B ? x : -INFINITY;
+        }
+    };
+    if (sb0 < sb1) load_smax(sb0);
+    const int prev = active ? prev_token(a, j, bme, vb == 0) : 0;
+    if (lhalf == 0) s_thr[wave][lrow] = -INFINITY;
+    wait_lds_reads();
+    wait_vmcnt<0>();   // the bound's copies, the slab maxima and the previous tokens
+    block_barrier();
+
+    // Skip threshold of this lane's block (lanes 0-31), from the KL-th largest
+    // bin and the global bound Bg of the Markov term.
+    {
+        const float kth = s_kth[nbw * 32 + lrow];
+        const float bg = sqrtf(__uint_as_float(s_w2n2[0])) * sqrtf(__uint_as_float(s_w1n2[0]));
+        const float skip = kth - 2.0f * bg * 1.001f - 2e-4f * (1.0f + fabsf(kth));
+        if (lhalf == 0) s_skip[wave][lrow] = skip;
+    }
+
+    // Per-lane fixed part of the copies of a step: markov_w2 chunk (row offset
+    // within the step, rank chunk) and logits chunk (block row, column).
+    int w_row[W_INST > 0 ? W_INST : 1], w_k[W_INST > 0 ? W_INST : 1], l_row[L_INST], l_col[L_INST];
+#pragma unroll
+    for (int i = 0; i < W_INST; ++i) {
+        const int slot = i * 64 + lane, row = slot / WRd;
+        const int c = (slot % WRd) ^ swz_rows<WR>(row);
+        w_row[i] = row;
+        w_k[i] = c * 8 < r ? c * 8 : 0;   // rank padding: any valid chunk
+    }
+#pragma unroll
+    for (int i = 0; i < L_INST; ++i) {
+        const int slot = i * 64 + lane, row = slot / LR;
+        l_row[i] = row;
+        l_col[i] = 4 * ((slot % LR) ^ swz_rows<LR>(row));
+    }
+    lds_char* ring_dma = (lds_char*)(lds_ptr)&ring[wave][0][0];
+    asm volatile("" : "+s"(ring_dma));
+    typedef const volatile __attribute__((address_space(3))) float lds_vfloat;
+    lds_vfloat* thr_v = (lds_vfloat*)&s_thr[0][0];
+
+    int my_slab = 0;          // lane k: slab of entry k of the pass's list
+    uint32_t my_need = 0u;    // and its block mask
+    // Step t of the pass: slab entry t / 2, columns v0 .. v0 + 31.
+    auto step_slab = [&](int t) __attribute__((always_inline)) {
+        return __builtin_amdgcn_readlane(my_slab, t >> 1);
+    };
+    auto step_need = [&](int t) __attribute__((always_inline)) {
+        return (uint32_t)__builtin_amdgcn_readlane((int)my_need, t >> 1);
+    };
+    auto copy = [&](bool w, const void* p, int st, int slot0) __attribute__((always_inline)) {
+        lds_ptr d = (lds_ptr)(ring_dma + (st * STAGE + slot0) * 16);
+        if (w) __builtin_amdgcn_global_load_lds(p, d, 16, 0, 0);
+        else __builtin_amdgcn_global_load_lds(p, d, 16, 0, kLoadNT);
+    };
+    const void* dummy = a.smax;
+    auto issue = [&](int st, int t) __attribute__((always_inline)) {
+        const int v0 = step_slab(t) * kSlabCols + (t & 1) * 32;
+        const uint32_t need = step_need(t);
+#pragma unroll
+        for (int i = 0; i < W_INST; ++i) {
+            const int row = min(v0 + w_row[i], V - 1);   // columns past V: row V - 1, never scored
+            copy(true, a.w2 + (long)row * r + w_k[i], st, i * 64);
+        }
+#pragma unroll
+        for (int i = 0; i < L_INST; ++i) {
+            const int b = gbase + l_row[i];
+            const int col = min(v0 + l_col[i], V - 4);
+            const void* p = ((need >> l_row[i]) & 1u)
+                                ? (const void*)(a.logits + ((long)b * a.n_pred + j) * V + col)
+                                : dummy;
+            copy(false, p, st, W_SLOTS + i * 64);
+        }
+    };
+
+    u32x4 u[RS > 0 ? RS : 1];
+    bool have_u = false;
+    float tau = -INFINITY;   // the block's top-k bound (with its own markov_w1 row)
+    u64 list[KL];
+#pragma unroll
+    for (int i = 0; i < KL; ++i) list[i] = 0ull;
+
+    auto score = [&](int st_, f32x16& acc) __attribute__((always_inline)) {
+        const u32x4* stg = ring[wave][st_];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int c = 2 * q + lhalf;
+            const int lr = lrow < LROWS ? lrow : 0;
+            f32x4 x = __builtin_bit_cast(f32x4, stg[W_SLOTS + lr * LR + (c ^ swz_rows<LR>(lr))]);
+            if (LROWS < 32 && lrow >= LROWS) x = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[4 * q + e] = x[e];
+        }
+#pragma unroll
+        for (int s = 0; s < RS; ++s) {
+            const u32x4 w = stg[lrow * WR + ((2 * s + lhalf) ^ swz_rows<WR>(lrow))];
+            acc = mfma32x32x16(w, u[s], acc);
+        }
+    };
+    auto consume = [&](int t, const f32x16& acc) __attribute__((always_inline)) {
+        const int vt = step_slab(t) * kSlabCols + (t & 1) * 32;
+        // this lane's block is streamed in this slab
+        const bool on = active && ((step_need(t) >> lrow) & 1u);
+        float z[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) z[e] = acc[e];
+        const int vlane = vt + 4 * lhalf;
+        if (vt + 32 > V) {
+            // the ragged last step: plain inserts of the columns inside V
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int v = vlane + 8 * (e >> 2) + (e & 3);
+                topk_insert<KL>(list, (on && v < V) ? make_key(z[e], v) : 0ull);
+            }
+        } else if constexpr (KL == 1) {
+            float best = z[0];
+            int be = 0;
+#pragma unroll
+            for (int e = 1; e < 16; ++e) {
+                const bool gt = z[e] > best;
+                best = gt ? z[e] : best;
+                be = gt ? e : be;
+            }
+            const u64 key = make_key(best, vlane + 8 * (be >> 2) + (be & 3));
+            if (on && key > list[0]) list[0] = key;
+        } else {
+            // filtered inserts, as in chain_step_wave
+            float sa[KL], sb[KL];
+#pragma unroll
+            for (int i = 0; i < KL; ++i) {
+                sa[i] = list[i] != 0ull ? key_score(list[i]) : -INFINITY;
+                sb[i] = __shfl_xor(sa[i], 32, kWave);
+            }
+            float thr = fmaxf(sa[KL - 1], sb[KL - 1]);
+#pragma unroll
+            for (int i = 1; i < KL; ++i) thr = fmaxf(thr, fminf(sa[i - 1], sb[KL - 1 - i]));
+            thr = fmaxf(thr, tau);
+            if (lhalf == 0 && active) s_thr[wave][lrow] = thr;
+#pragma unroll
+            for (int w = 0; w < VW; ++w)
+                if (w != vb) thr = fmaxf(thr, thr_v[(nbw * VW + w) * 32 + lrow]);
+            float zmax = z[0];
+#pragma unroll
+            for (int e = 1; e < 16; ++e) zmax = fmaxf(zmax, z[e]);
+            if (__any(on && zmax >= thr)) {
+                unsigned hits = 0u;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) hits |= (z[e] >= thr ? 1u : 0u) << e;
+                if (!on) hits = 0u;
+                while (__any(hits != 0u)) {
+                    const bool has = hits != 0u;
+                    const int e = __builtin_ctz(hits | 0x10000u);
+                    hits &= hits - 1u;
+                    const u64 m0 = __builtin_amdgcn_ballot_w64((e & 1) != 0);
+                    const u64 m1 = __builtin_amdgcn_ballot_w64((e & 2) != 0);
+                    const u64 m2 = __builtin_amdgcn_ballot_w64((e & 4) != 0);
+                    const u64 m3 = __builtin_amdgcn_ballot_w64((e & 8) != 0);
+                    float s8[8], s4[4], s2[2];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) s8[i] = lane_select(z[2 * i + 1], z[2 * i], m0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) s4[i] = lane_select(s8[2 * i + 1], s8[2 * i], m1);
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) s2[i] = lane_select(s4[2 * i + 1], s4[2 * i], m2);
+                    const float ze = lane_select(s2[1], s2[0], m3);
+                    topk_insert<KL>(list, has ? make_key(ze, vlane + 8 * (e >> 2) + (e & 3)) : 0ull);
+                }
+            }
+        }
+    };
+
+    for (int pb = sb0; pb < sb1; pb += 64) {
+        if (pb != sb0) load_smax(pb);
+        // the need masks of the pass's slabs (lane k: slab pb + k)
+        uint32_t need = 0u;
+        if (pb + lane < sb1) {
+#pragma unroll
+            for (int k = 0; k < 32; ++k) need |= (sm[k] >= s_skip[wave][k] ? 1u : 0u) << k;
+            need &= exist;
+        }
+        // compact the slabs some block needs into entries 0 .. cnt - 1
+        const u64 bal = __builtin_amdgcn_ballot_w64(need != 0u);
+        const int cnt = __builtin_popcountll(bal);
+        if (need != 0u) {
+            const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+            s_slab[wave][pos] = pb + lane;
+            s_need[wave][pos] = need;
+        }
+        wait_lds_reads();
+        my_slab = lane < cnt ? s_slab[wave][lane] : 0;
+        my_need = lane < cnt ? s_need[wave][lane] : 0u;
+        const int n = 2 * cnt;   // 32-column steps of the pass
+        if (n == 0) continue;
+
+        // Prologue: step 0, the markov_w1 rows of prev into stage NS - 1 (the
+        // first pass with work only), steps 1 .. NS - 2; then step NS - 1 into
+        // stage NS - 1 once the rows are in registers. A stage past the last
+        // step gets a second copy of it (no iteration reads it), so the number
+        // of copies in flight is fixed.
+        issue(0, 0);
+        const bool first = !have_u;
+        if (first) {
+#pragma unroll
+            for (int s = 0; s < RS; ++s) {
+                const int k0 = s * 16 + lhalf * 8;
+                __builtin_amdgcn_global_load_lds((const void*)(a.w1 + (long)prev * r + (k0 < r ? k0 : 0)),
+                                                 (lds_ptr)(ring_dma + ((NS - 1) * STAGE + s * 64) * 16), 16, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int t = 1; t < NS - 1; ++t) issue(t, min(t, n - 1));
+        wait_vmcnt<(NS - 2) * LW>();
+        asm volatile("" ::: "memory");
+        if (first) {
+#pragma unroll
+            for (int s = 0; s < RS; ++s) {
+                u[s] = ring[wave][NS - 1][s * 64 + lane];
+                if (s * 16 + lhalf * 8 >= r) u[s] = u32x4{0u, 0u, 0u, 0u};
+            }
+            have_u = true;
+            if constexpr (KL > 1) {
+                const float un2 = w1_norm2<RS>(u);
+                tau = chain_bound(s_kth[nbw * 32 + lrow], __uint_as_float(s_w2n2[0]), un2);
+            }
+        }
+        asm volatile("" ::: "memory");
+        wait_lds_reads();
+        asm volatile("" ::: "memory");
+        issue(NS - 1, min(NS - 1, n - 1));
+
+        auto step_tile = [&](int it, int& st, const f32x16& cur, f32x16& nxt) __attribute__((always_inline)) {
+            if (it + NS < n) {
+                wait_lds_reads();
+                asm volatile("" ::: "memory");
+                issue(st, it + NS);
+            }
+            const int nst = st + 1 == NS ? 0 : st + 1;
+            if (it + 1 < n) {
+                const int newer = n >= NS ? min(NS - 1, n - 2 - it) : NS - 2 - it;
+                wait_stages<LW, NS - 1>(newer);
+                asm volatile("" ::: "memory");
+                score(nst, nxt);
+            }
+            consume(it, cur);
+            st = nst;
+        };
+        int st = 0;
+        f32x16 S0, S1;
+        score(0, S0);
+        for (int it = 0; it < n; it += 2) {
+            step_tile(it, st, S0, S1);
+            if (it + 1 < n) step_tile(it + 1, st, S1, S0);
+        }
+        // every copy of the pass (extra ones included) has landed and been
+        // read before the next pass refills the ring
+        wait_vmcnt<0>();
+        wait_lds_reads();
+        asm volatile("" ::: "memory");
+    }
+
+    // Merge: the lane pair that holds the same block, then the VW waves of
+    // the block group through LDS (each wave's list in its own ring).
+    {
+        u64 other[KL];
+#pragma unroll
+        for (int i = 0; i < KL; ++i) other[i] = shfl_xor_u64(list[i], 32);
+#pragma unroll
+        for (int i = 0; i < KL; ++i) topk_insert<KL>(list, other[i]);
+    }
+    wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
+    if (lhalf == 0) {
+        u64* s_list = reinterpret_cast<u64*>(&ring[wave][0][0]);
+#pragma unroll
+        for (int i = 0; i < KL; ++i) s_list[lrow * KL + i] = list[i];
+    }
+    __syncthreads();
+    if (vb == 0 && lhalf == 0 && active) {
+#pragma unroll
+        for (int w = 1; w < VW; ++w) {
+            const u64* o = reinterpret_cast<const u64*>(&ring[wave + w][0][0]);
+#pragma unroll
+            for (int i = 0; i < KL; ++i) topk_insert<KL>(list, o[lrow * KL + i]);
+        }
+        const int g = blockIdx.x;
         if (a.top_k > 1) {
             u64* p = a.partials + (((long)j * B + bme) * a.nwg + g) * a.top_k;
 #pragma unroll
@@ -1260,6 +1664,47 @@ hipError_t step_wave_rows(const ChainArgs& a, int j, dim3 grid, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Pruned form: as many stages as fit its budgets (chain_sparse_per_cu), at most 8.
+template <int RS, int LROWS, int WPC>
+constexpr int chain_sparse_stages() {
+    const int n = (WPC == 2 ? kChainSparseBudget2 : kChainSparseBudget1) / (4 * chain_wave_stage_bytes(RS, LROWS));
+    return n > 8 ? 8 : n;
+}
+
+template <int NB, int KL, int LROWS>
+hipError_t step_sparse_rows(const ChainArgs& a, int j, dim3 grid, hipStream_t s) {
+    const int rs = chain_wave_rank(a.r);
+    const bool two = chain_sparse_per_cu(a.B, a.r, a.top_k) == 2;
+#define DSPARK_STEP(RSV, WPCV)                                                                     \
+    hipLaunchKernelGGL((chain_step_sparse<NB, KL, RSV, chain_sparse_stages<RSV, LROWS, WPCV>(), LROWS>), \
+                       grid, dim3(256), 0, s, a, j);
+#define DSPARK_RANK(RSV)                                                                         \
+    if constexpr (LROWS < 32 && chain_sparse_stages<RSV, LROWS, 2>() >= 2) {                     \
+        if (two) { DSPARK_STEP(RSV, 2) }                                                         \
+        else { DSPARK_STEP(RSV, 1) }                                                             \
+    } else {                                                                                     \
+        DSPARK_STEP(RSV, 1)                                                                      \
+    }
+    if (rs == 0) { DSPARK_RANK(0) }
+    else if (rs == 2) { DSPARK_RANK(2) }
+    else if (rs == 4) { DSPARK_RANK(4) }
+    else if (rs == 8) { DSPARK_RANK(8) }
+    else return hipErrorInvalidValue;   // chain_sparse excludes wider ranks
+#undef DSPARK_RANK
+#undef DSPARK_STEP
+    return hipGetLastError();
+}
+
+template <int NB, int KL>
+hipError_t step_sparse(const ChainArgs& a, int j, dim3 grid, hipStream_t s) {
+    if constexpr (NB == 1 && KL <= 4) {
+        const int lr = chain_wave_rows(a.B, a.top_k);
+        if (lr == 8) return step_sparse_rows<NB, KL, 8>(a, j, grid, s);
+        if (lr == 16) return step_sparse_rows<NB, KL, 16>(a, j, grid, s);
+    }
+    return step_sparse_rows<NB, KL, 32>(a, j, grid, s);
+}
+
 template <int NB, int KL>
 hipError_t step_wave(const ChainArgs& a, int j, dim3 grid, hipStream_t s) {
     if constexpr (NB == 1 && KL <= 4) {
@@ -1285,6 +1730,12 @@ hipError_t step_form(const ChainArgs& a, int j, dim3 grid, ChainForm f, hipStrea
 
 template <int NB>
 hipError_t step_kl(const ChainArgs& a, int j, dim3 grid, ChainForm f, hipStream_t s) {
+    if (a.sparse) {
+        if (a.top_k == 1) return step_sparse<NB, 1>(a, j, grid, s);
+        if (a.top_k <= 4) return step_sparse<NB, 4>(a, j, grid, s);
+        if (a.top_k <= 8) return step_sparse<NB, 8>(a, j, grid, s);
+        return step_sparse<NB, 16>(a, j, grid, s);
+    }
     if (a.top_k == 1) return step_form<NB, 1>(a, j, grid, f, s);
     if (a.top_k <= 4) return step_form<NB, 4>(a, j, grid, f, s);
     if (a.top_k <= 8) return step_form<NB, 8>(a, j, grid, f, s);
@@ -1295,11 +1746,19 @@ hipError_t step_kl(const ChainArgs& a, int j, dim3 grid, ChainForm f, hipStream_
 
 hipError_t launch_chain_init(const ChainArgs& a, hipStream_t stream) {
     const int nw = a.n_pred * kWinnerWays * a.wstride;   // < 2^31 (checked on the host)
-    const int nb = a.bins ? a.B * a.n_pred * kBoundBins : 0;
-    int n = nw > a.B ? nw : a.B;
-    n = n > nb ? n : nb;
+    const int n = nw > a.B ? nw : a.B;
     hipLaunchKernelGGL(chain_init, dim3((n + 255) / 256), dim3(256), 0, stream, a.winners, nw,
-                       a.flags, a.lengths, a.B, a.n_pred, a.bins, nb, a.w2n2);
+                       a.flags, a.lengths, a.B, a.n_pred, a.w2n2, a.w1n2);
+    return hipGetLastError();
+}
+
+hipError_t launch_row_kth(const ChainArgs& a, hipStream_t stream) {
+    const int M = a.B * a.n_pred, nslab = (a.V + a.slab_cols - 1) / a.slab_cols;
+    const dim3 grid(M), block(256);
+    if (a.top_k == 1) hipLaunchKernelGGL(row_kth<1>, grid, block, 0, stream, a.smax, nslab, a.kth);
+    else if (a.top_k <= 4) hipLaunchKernelGGL(row_kth<4>, grid, block, 0, stream, a.smax, nslab, a.kth);
+    else if (a.top_k <= 8) hipLaunchKernelGGL(row_kth<8>, grid, block, 0, stream, a.smax, nslab, a.kth);
+    else hipLaunchKernelGGL(row_kth<16>, grid, block, 0, stream, a.smax, nslab, a.kth);
     return hipGetLastError();
 }
 

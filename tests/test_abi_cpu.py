@@ -40,7 +40,8 @@ def test_status_strings(lib):
 
 def test_workspace_bytes_layout(lib):
     # [256 B flags][n_pred*8*roundup(B, 32)*8 winners (8 ways per block), 256-aligned]
-    # [B*n_pred*16*4 row-maximum bins, 256-aligned, top_k > 1]
+    # [B*n_pred*4 k-th slab maxima, 256-aligned]
+    # [B*n_pred*ceil(V/64)*4 slab maxima, 256-aligned]
     # [n_pred*B*nwg*top_k*8 partials, 256-aligned, top_k > 1]
     def al(x):
         return (x + 255) // 256 * 256
@@ -50,8 +51,9 @@ def test_workspace_bytes_layout(lib):
         # chain workgroups: pipelined kernel (V % 4 == 0) runs at most min(ceil(V/64), 512)
         # (two per CU in its two-stage form), the direct kernel one per 128 columns
         nwg = min((V + 63) // 64, 512) if V % 4 == 0 else (V + 127) // 128
-        want = (256 + al(n * 8 * ((B + 31) // 32 * 32) * 8)
-                + (al(B * n * 16 * 4) + al(n * B * nwg * k * 8) if k > 1 else 0))
+        Bp = (B + 31) // 32 * 32
+        want = (256 + al(n * 8 * Bp * 8) + al(B * n * 4) + al(B * n * ((V + 63) // 64) * 4)
+                + (al(n * B * nwg * k * 8) if k > 1 else 0))
         assert lib.dspark_workspace_bytes(B, L, V, k, lay) == want
 
 
