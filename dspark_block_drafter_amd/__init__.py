@@ -28,6 +28,8 @@ ERR_INVALID_ARG = -1
 ERR_UNSUPPORTED = -2
 ERR_WORKSPACE = -3
 ERR_HIP = -4
+ERR_SCRATCH = -5
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 FLAG_BAD_ANCHOR = 1
 FLAG_INTERNAL = 2
@@ -36,8 +38,8 @@ FLAG_BAD_D2T = 4
 MAX_TOP_K = 16
 MAX_RANK = 256
 
-EXPORTS = ("dspark_workspace_bytes", "dspark_propose", "dspark_propose_marked", "dspark_logits",
-           "dspark_chain",
+EXPORTS = ("dspark_workspace_bytes", "dspark_propose", "dspark_propose_marked",
+           "dspark_propose_noalloc", "dspark_logits", "dspark_chain",
            "dspark_propose_d2t", "dspark_propose_adaptive", "dspark_verify", "dspark_read_flags",
            "dspark_status_string")
 
@@ -72,6 +74,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dspark_propose.restype = _i
     lib.dspark_propose_marked.argtypes = lib.dspark_propose.argtypes + [_vp, _vp, _vp]
     lib.dspark_propose_marked.restype = _i
+    lib.dspark_propose_noalloc.argtypes = [_vp, _i, _vp, _vp, _vp, _vp, _vp, _vp,
+                                           _i, _i, _i, _i, _i, _i, _i, _f,
+                                           _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+    lib.dspark_propose_noalloc.restype = _i
     lib.dspark_logits.argtypes = [_vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]
     lib.dspark_logits.restype = _i
     lib.dspark_chain.argtypes = [_vp, _vp, _i, _vp, _vp, _vp, _vp,
@@ -216,6 +222,35 @@ def propose(hidden, lm_head, markov_w1, markov_w2, anchors, *, layout="anchor_fi
         st = lib.dspark_propose_marked(*args, *[_event_handle(e) for e in marks])
     if st != OK:
         raise DsparkError(st, "dspark_propose_marked" if marks is not None else "dspark_propose")
+    return out
+
+
+def propose_noalloc(hidden, lm_head, markov_w1, markov_w2, anchors, *, layout="anchor_first",
+                    top_k=1, p_min=0.0, lm_head_bias=None, conf_w=None,
+                    out: Optional[Outputs] = None, stream=None) -> Outputs:
+    """Run dspark_propose_noalloc (the library's static scratch as workspace;
+    ``out.workspace`` is not used). Returns the Outputs holding the results."""
+    torch = _torch()
+    lib = load_library()
+    B, L, H = hidden.shape
+    V = lm_head.shape[0]
+    r = 0 if markov_w1 is None else markov_w1.shape[1]
+    _check_dev("hidden", hidden, hidden.dtype)
+    _check_dev("lm_head", lm_head, torch.bfloat16, (V, H))
+    _check_dev("lm_head_bias", lm_head_bias, torch.float32, (V,))
+    _check_dev("markov_w1", markov_w1, torch.bfloat16, (V, r))
+    _check_dev("markov_w2", markov_w2, torch.bfloat16, (V, r))
+    _check_dev("conf_w", conf_w, torch.bfloat16, (H,))
+    _check_dev("anchors", anchors, torch.int32, (B,))
+    if out is None:
+        out = Outputs(B, L, V, top_k, layout, hidden.device)
+    st = lib.dspark_propose_noalloc(
+        _ptr(hidden), _hidden_dtype(hidden), _ptr(lm_head), _ptr(lm_head_bias), _ptr(markov_w1),
+        _ptr(markov_w2), _ptr(conf_w), _ptr(anchors), B, L, H, V, r, LAYOUTS[layout], top_k,
+        float(p_min), _ptr(out.logits), _ptr(out.tokens), _ptr(out.candidates),
+        _ptr(out.cand_logits), _ptr(out.conf), _ptr(out.lengths), _stream(hidden, stream))
+    if st != OK:
+        raise DsparkError(st, "dspark_propose_noalloc")
     return out
 
 

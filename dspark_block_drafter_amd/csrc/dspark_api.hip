@@ -11,6 +11,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/dspark.h"
 #include "kernels.hpp"
 
@@ -288,6 +291,40 @@ int propose_impl(const void* hidden, int hidden_dtype, const uint16_t* lm_head,
 
 }  // namespace
 
+// Scratch of dspark_propose_noalloc: the workspace of one call in a
+// file-scope device array. Every GPU the library runs on holds its own copy
+// (DSPARK_NOALLOC_SCRATCH_BYTES) from the first use until the process ends.
+// Host code reaches it only through the address hipGetSymbolAddress returns
+// for the current device (the array's name on the host is a stand-in).
+static __device__ __align__(256) unsigned char scratch[DSPARK_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];   // per device: the device address of scratch
+std::mutex g_scratch_mu;
+
+// The address of the current device's scratch, taken once per device.
+int scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return DSPARK_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return DSPARK_ERR_UNSUPPORTED;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+                return DSPARK_ERR_HIP;
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return DSPARK_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t dspark_workspace_bytes(int B, int L, int V, int top_k, int layout) {
@@ -349,6 +386,31 @@ int dspark_propose(const void* hidden, int hidden_dtype, const uint16_t* lm_head
                         anchors, B, L, H, V, r, layout, top_k, p_min, logits, workspace,
                         workspace_bytes, tokens, candidates, cand_logits, conf, lengths,
                         static_cast<hipStream_t>(stream), nullptr, nullptr, nullptr);
+}
+
+int dspark_propose_noalloc(const void* hidden, int hidden_dtype, const uint16_t* lm_head,
+                           const float* lm_head_bias, const uint16_t* markov_w1,
+                           const uint16_t* markov_w2, const uint16_t* conf_w,
+                           const int32_t* anchors, int B, int L, int H, int V, int r, int layout,
+                           int top_k, float p_min, float* logits, int32_t* tokens,
+                           int32_t* candidates, float* cand_logits, float* conf, int32_t* lengths,
+                           void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // Validation first (a call without a workspace stops at the workspace
+    // check, with nothing enqueued, when every other argument is valid).
+    int st = propose_impl(hidden, hidden_dtype, lm_head, lm_head_bias, markov_w1, markov_w2, conf_w,
+                          anchors, B, L, H, V, r, layout, top_k, p_min, logits, nullptr, 0, tokens,
+                          candidates, cand_logits, conf, lengths, s, nullptr, nullptr, nullptr);
+    if (st != DSPARK_ERR_WORKSPACE) return st;
+    if (dspark_workspace_bytes(B, L, V, top_k, layout) > (size_t)DSPARK_NOALLOC_SCRATCH_BYTES)
+        return DSPARK_ERR_SCRATCH;
+    void* ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != DSPARK_OK) return st;
+    return propose_impl(hidden, hidden_dtype, lm_head, lm_head_bias, markov_w1, markov_w2, conf_w,
+                        anchors, B, L, H, V, r, layout, top_k, p_min, logits, ws,
+                        (size_t)DSPARK_NOALLOC_SCRATCH_BYTES, tokens, candidates, cand_logits, conf,
+                        lengths, s, nullptr, nullptr, nullptr);
 }
 
 int dspark_propose_marked(const void* hidden, int hidden_dtype, const uint16_t* lm_head,
@@ -470,6 +532,8 @@ const char* dspark_status_string(int status) {
         case DSPARK_ERR_UNSUPPORTED: return "unsupported size or alignment";
         case DSPARK_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
         case DSPARK_ERR_HIP: return "HIP runtime error while enqueuing";
+        case DSPARK_ERR_SCRATCH:
+            return "sizes need more workspace than the allocation-free entry point's static scratch";
         default: return "unknown status";
     }
 }

@@ -76,7 +76,8 @@ typedef enum {
     DSPARK_ERR_INVALID_ARG = -1, /* a size, pointer, enum or p_min is not acceptable      */
     DSPARK_ERR_UNSUPPORTED = -2, /* valid, but outside what the kernels implement          */
     DSPARK_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than dspark_workspace_bytes */
-    DSPARK_ERR_HIP = -4          /* the HIP runtime reported an error while enqueuing     */
+    DSPARK_ERR_HIP = -4,         /* the HIP runtime reported an error while enqueuing     */
+    DSPARK_ERR_SCRATCH = -5      /* dspark_propose_noalloc: sizes exceed its static scratch */
 } dspark_status;
 /* An error left pending in the HIP runtime by an earlier call outside the
  * library is cleared when an entry point starts enqueuing; only errors of the
@@ -152,6 +153,33 @@ int dspark_propose(const void* hidden, int hidden_dtype, const uint16_t* lm_head
                    float* logits, void* workspace, size_t workspace_bytes, int32_t* tokens,
                    int32_t* candidates, float* cand_logits, float* conf, int32_t* lengths,
                    void* stream);
+
+/*
+ * dspark_propose for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same launches and results, with the workspace taken from a static
+ * device array of DSPARK_NOALLOC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on (from the first use until the process ends). The
+ * call allocates and frees nothing. The current device's array is used
+ * (hipGetDevice; `stream` must belong to that device); its address is taken
+ * once per device with hipGetSymbolAddress.
+ *
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap on one GPU (other streams, other threads)
+ * race and must be serialised by the caller. Every call clears what must
+ * start at zero. Sizes whose workspace (dspark_workspace_bytes) exceeds the
+ * array return DSPARK_ERR_SCRATCH with nothing enqueued. The device-side
+ * flags (DSPARK_FLAG_*) stay in the array and are not reported.
+ * Every other argument is as in dspark_propose. Returns a dspark_status.
+ */
+#define DSPARK_NOALLOC_SCRATCH_BYTES (64u << 20)
+int dspark_propose_noalloc(const void* hidden, int hidden_dtype, const uint16_t* lm_head,
+                           const float* lm_head_bias, const uint16_t* markov_w1,
+                           const uint16_t* markov_w2, const uint16_t* conf_w,
+                           const int32_t* anchors, int B, int L, int H, int V, int r, int layout,
+                           int top_k, float p_min, float* logits, int32_t* tokens,
+                           int32_t* candidates, float* cand_logits, float* conf, int32_t* lengths,
+                           void* stream);
 
 /*
  * dspark_propose with three HIP events (hipEvent_t, each may be NULL)

@@ -177,3 +177,26 @@ def test_read_flags_rejects_null(lib):
 def test_binding_refuses_missing_library(tmp_path):
     with pytest.raises(ImportError):
         dsp.load_library(str(tmp_path / "libdspark.so"))
+
+
+def test_noalloc_validates_before_anything(lib):
+    """dspark_propose_noalloc rejects bad arguments like dspark_propose, and
+    sizes whose workspace exceeds its static scratch with DSPARK_ERR_SCRATCH,
+    all before any HIP call (no GPU here)."""
+    def call(**kw):
+        a = dict(hidden=P, hidden_dtype=0, lm_head=P, bias=None, w1=P, w2=P, conf_w=P, anchors=P,
+                 B=2, L=4, H=64, V=512, r=8, layout=0, top_k=2, p_min=0.5, logits=P, tokens=P,
+                 cand=P, cand_logits=P, conf=P, lengths=P, stream=None)
+        a.update(kw)
+        return lib.dspark_propose_noalloc(
+            a["hidden"], a["hidden_dtype"], a["lm_head"], a["bias"], a["w1"], a["w2"], a["conf_w"],
+            a["anchors"], a["B"], a["L"], a["H"], a["V"], a["r"], a["layout"], a["top_k"],
+            ctypes.c_float(a["p_min"]), a["logits"], a["tokens"], a["cand"], a["cand_logits"],
+            a["conf"], a["lengths"], a["stream"])
+    assert call(B=0) == dsp.ERR_INVALID_ARG
+    assert call(top_k=17) == dsp.ERR_INVALID_ARG
+    assert call(tokens=None) == dsp.ERR_INVALID_ARG
+    assert call(H=12) == dsp.ERR_UNSUPPORTED
+    assert call(B=512, L=64, V=248320, top_k=4) == dsp.ERR_SCRATCH
+    assert dsp.workspace_bytes(512, 64, 248320, 4) > dsp.NOALLOC_SCRATCH_BYTES
+    assert "static scratch" in dsp.status_string(dsp.ERR_SCRATCH)
