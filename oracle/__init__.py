@@ -42,6 +42,7 @@ def build(src: str = SRC_PATH, out: str = LIB_PATH) -> str:
 
 _LIB: Optional[ctypes.CDLL] = None
 
+_u8p = ctypes.POINTER(ctypes.c_uint8)
 _u16p = ctypes.POINTER(ctypes.c_uint16)
 _f32p = ctypes.POINTER(ctypes.c_float)
 _f64p = ctypes.POINTER(ctypes.c_double)
@@ -89,6 +90,16 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_propose_block_gated.restype = _i
     lib.oracle_verify.argtypes = [_i32p, _i32p, _i32p, _i, _i, _i, _i, _i32p, _i64p]
     lib.oracle_verify.restype = _i
+    lib.oracle_f16_value.argtypes = [ctypes.c_uint16]
+    lib.oracle_f16_value.restype = ctypes.c_double
+    lib.oracle_q4_dequant_row.argtypes = [_u8p, _i, ctypes.c_long, _f64p]
+    lib.oracle_q4_dequant_row.restype = _i
+    lib.oracle_block_logits_q4.argtypes = [_vp, _i, _u8p, _f32p, _i, _i, _i, _i, _i, _f64p]
+    lib.oracle_block_logits_q4.restype = _i
+    lib.oracle_propose_block_q4.argtypes = [_vp, _i, _u8p, _f32p, _u16p, _u16p, _u16p, _i32p,
+                                            _i, _i, _i, _i, _i, _i, ctypes.c_float, _i, _f64p,
+                                            _i32p, _i32p, _f32p, _f32p, _i32p]
+    lib.oracle_propose_block_q4.restype = _i
     return lib
 
 
@@ -130,6 +141,8 @@ class Oracle:
 
     # --- method steps -----------------------------------------------------
     def block_logits(self, inp, b: int) -> np.ndarray:
+        if hasattr(inp, "lm_head_q4"):
+            return self.block_logits_q4(inp, b)
         c = inp.cfg
         z = np.empty((c.n_pred, c.V), dtype=np.float64)
         st = self.lib.oracle_block_logits(
@@ -283,11 +296,59 @@ class Oracle:
         return {"logits": z, "tokens": tokens, "candidates": cand, "cand_logits": cval,
                 "conf": conf, "length": int(length[0])}
 
+    # --- quantized head (q4) -----------------------------------------------
+    def f16_value(self, bits: int) -> float:
+        return float(self.lib.oracle_f16_value(ctypes.c_uint16(bits)))
+
+    def q4_dequant_row(self, q4: np.ndarray, H: int, v: int) -> np.ndarray:
+        """Row v of a q4 head (uint8 [V, H/32*18] GGUF blocks) as exact float64."""
+        q4 = np.ascontiguousarray(q4, dtype=np.uint8)
+        w = np.empty(H, dtype=np.float64)
+        st = self.lib.oracle_q4_dequant_row(_p(q4, _u8p), H, int(v), _p(w, _f64p))
+        if st != 0:
+            raise ValueError("oracle_q4_dequant_row rejected its arguments")
+        return w
+
+    def block_logits_q4(self, qinp, b: int) -> np.ndarray:
+        """Projections of block b through the q4 head of ``qinp`` (synthetic.Q4Inputs)."""
+        c = qinp.cfg
+        z = np.empty((c.n_pred, c.V), dtype=np.float64)
+        st = self.lib.oracle_block_logits_q4(
+            qinp.hidden.ctypes.data, int(qinp.hidden_f32), _p(qinp.lm_head_q4, _u8p),
+            _p(qinp.lm_head_bias, _f32p), c.L, c.H, c.V, c.i_first_pred, b, _p(z, _f64p))
+        if st != 0:
+            raise ValueError("oracle_block_logits_q4 rejected its arguments")
+        return z
+
+    def propose_block_q4(self, qinp, b: int, keep_logits: bool = True) -> dict:
+        c = qinp.cfg
+        n, k = c.n_pred, c.top_k
+        z = np.empty((n, c.V), dtype=np.float64) if keep_logits else None
+        tokens = np.empty(n, dtype=np.int32)
+        cand = np.empty((n, k), dtype=np.int32)
+        cval = np.empty((n, k), dtype=np.float32)
+        conf = np.empty(n, dtype=np.float32)
+        length = np.zeros(1, dtype=np.int32)
+        st = self.lib.oracle_propose_block_q4(
+            qinp.hidden.ctypes.data, int(qinp.hidden_f32), _p(qinp.lm_head_q4, _u8p),
+            _p(qinp.lm_head_bias, _f32p), _p(qinp.markov_w1, _u16p), _p(qinp.markov_w2, _u16p),
+            _p(qinp.conf_w, _u16p), _p(qinp.anchors, _i32p), c.L, c.H, c.V, c.r,
+            c.i_first_pred, k, ctypes.c_float(c.p_min), b,
+            _p(z, _f64p) if z is not None else ctypes.cast(None, _f64p),
+            _p(tokens, _i32p), _p(cand, _i32p), _p(cval, _f32p), _p(conf, _f32p),
+            _p(length, _i32p))
+        if st != 0:
+            raise ValueError("oracle_propose_block_q4 rejected its arguments")
+        return {"logits": z, "tokens": tokens, "candidates": cand, "cand_logits": cval,
+                "conf": conf, "length": int(length[0])}
+
     def propose(self, inp, blocks: Optional[Sequence[int]] = None, keep_logits: bool = True) -> dict:
-        """Oracle outputs for the listed blocks (all blocks by default), stacked."""
+        """Oracle outputs for the listed blocks (all blocks by default), stacked
+        (a synthetic.Q4Inputs goes through the q4 head)."""
         c = inp.cfg
         blocks = list(range(c.B)) if blocks is None else list(blocks)
-        outs = [self.propose_block(inp, b, keep_logits) for b in blocks]
+        one = self.propose_block_q4 if hasattr(inp, "lm_head_q4") else self.propose_block
+        outs = [one(inp, b, keep_logits) for b in blocks]
         res = {
             "blocks": np.array(blocks, dtype=np.int64),
             "tokens": np.stack([o["tokens"] for o in outs]),

@@ -58,6 +58,17 @@
  * i_first_pred = 1) (llama.cpp PR #26275, first commit message and
  * "Format differences").
  *
+ * Quantized head (q4): the drafter the pages validate on the device is a
+ * requantized GGUF with 4-bit weights (lucebox PR #626, "Drafter"), but they
+ * never spell out the block format. The reading taken here is GGUF's plain
+ * 4-bit type: every row of lm_head is H/32 blocks of 18 bytes, each an IEEE
+ * binary16 scale d (little-endian) followed by 16 bytes of codes; byte j of
+ * the codes carries element j of the block in its low nibble and element
+ * j + 16 in its high nibble, and an element with code q is worth d * (q - 8).
+ * The projection is then the plain one over those exact values (PARITY
+ * PINNED by a hand-decoded golden row, numpy, and equality with the bf16
+ * path when every decoded weight is a bf16 value).
+ *
  * Arithmetic: bf16 operands are decoded exactly, every sum is accumulated in
  * double precision in increasing index order (a bf16*bf16 product is exact in
  * double), and a value is rounded once to float only where the contract hands
@@ -327,6 +338,25 @@ int oracle_truncate(const float* conf, int n_pred, float p_min)
     return n_pred;
 }
 
+/* Chain, confidence and truncation of block b over its projections z
+ * [n_pred][V]; with no conf_w, conf = 1 and length = n_pred. */
+static int finish_block(const double* z, const void* hidden, int hidden_is_f32,
+                        const uint16_t* w1, const uint16_t* w2, const uint16_t* conf_w,
+                        const int32_t* anchors, int L, int H, int V, int r, int i_first_pred,
+                        int top_k, float p_min, int b, int32_t* tokens, int32_t* cand,
+                        float* cand_val, float* conf, int32_t* length)
+{
+    const int n_pred = L - i_first_pred;
+    int st = oracle_block_chain(z, w1, w2, V, r, anchors[b], n_pred, top_k, tokens, cand, cand_val);
+    if (st == ORACLE_OK) {
+        for (int j = 0; j < n_pred; ++j)
+            conf[j] = conf_w ? oracle_conf(hidden, hidden_is_f32, conf_w, L, H, i_first_pred, b, j)
+                             : 1.0f;
+        *length = conf_w ? oracle_truncate(conf, n_pred, p_min) : n_pred;
+    }
+    return st;
+}
+
 /* Everything for block b. z (may be NULL) receives the projections
  * [n_pred][V]; with no conf_w, conf = 1 and length = n_pred. */
 int oracle_propose_block(const void* hidden, int hidden_is_f32, const uint16_t* lm_head,
@@ -342,13 +372,121 @@ int oracle_propose_block(const void* hidden, int hidden_is_f32, const uint16_t* 
         return ORACLE_ERR;
     int st = oracle_block_logits(hidden, hidden_is_f32, lm_head, bias, L, H, V, i_first_pred, b, zz);
     if (st == ORACLE_OK)
-        st = oracle_block_chain(zz, w1, w2, V, r, anchors[b], n_pred, top_k, tokens, cand, cand_val);
-    if (st == ORACLE_OK) {
-        for (int j = 0; j < n_pred; ++j)
-            conf[j] = conf_w ? oracle_conf(hidden, hidden_is_f32, conf_w, L, H, i_first_pred, b, j)
-                             : 1.0f;
-        *length = conf_w ? oracle_truncate(conf, n_pred, p_min) : n_pred;
+        st = finish_block(zz, hidden, hidden_is_f32, w1, w2, conf_w, anchors, L, H, V, r,
+                          i_first_pred, top_k, p_min, b, tokens, cand, cand_val, conf, length);
+    if (!z)
+        free(zz);
+    return st;
+}
+
+/* ---- quantized head (q4) ------------------------------------------------ */
+
+#define Q4_BLOCK 32
+#define Q4_BLOCK_BYTES 18
+
+/* Value of an IEEE binary16 bit pattern: sign, 5-bit exponent (bias 15),
+ * 10-bit fraction; exponent 0 holds zero and the subnormals. */
+static double f16_value(uint16_t bits)
+{
+    const int e = (bits >> 10) & 0x1f;
+    const int f = bits & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25);
+    return (bits & 0x8000u) ? -v : v;
+}
+
+double oracle_f16_value(uint16_t bits) { return f16_value(bits); }
+
+/* Row v of a q4 head as exact doubles w[0..H): block i of the row is bytes
+ * [18 i, 18 i + 18) of the row's H/32 * 18 bytes; its scale d is the
+ * binary16 in the first two bytes (low byte first), and code byte j (the
+ * bytes after the scale) gives element 32 i + j its low nibble and element
+ * 32 i + j + 16 its high nibble; an element is d * (code - 8), exact in
+ * double (an 11-bit significand times a 4-bit integer). */
+int oracle_q4_dequant_row(const uint8_t* q4, int H, long v, double* w)
+{
+    if (H <= 0 || H % Q4_BLOCK != 0 || v < 0)
+        return ORACLE_ERR;
+    const int nb = H / Q4_BLOCK;
+    const uint8_t* row = q4 + v * (long)nb * Q4_BLOCK_BYTES;
+    for (int i = 0; i < nb; ++i) {
+        const uint8_t* blk = row + (long)i * Q4_BLOCK_BYTES;
+        const double d = f16_value((uint16_t)(blk[0] | (blk[1] << 8)));
+        const uint8_t* qs = blk + 2;
+        for (int j = 0; j < 16; ++j) {
+            w[i * Q4_BLOCK + j] = d * (double)((int)(qs[j] & 0x0f) - 8);
+            w[i * Q4_BLOCK + j + 16] = d * (double)((int)(qs[j] >> 4) - 8);
+        }
     }
+    return ORACLE_OK;
+}
+
+/* Projection of the n_pred prediction rows of block b through a q4 head:
+ * z[j*V + v] = sum_h x_j[h] * w_v[h] (+ bias[v]) with w_v the decoded row v,
+ * summed in increasing h exactly as oracle_block_logits does. */
+int oracle_block_logits_q4(const void* hidden, int hidden_is_f32, const uint8_t* q4,
+                           const float* bias, int L, int H, int V, int i_first_pred, int b,
+                           double* z)
+{
+    int n_pred = L - i_first_pred;
+    if (n_pred <= 0 || H <= 0 || H % Q4_BLOCK != 0 || V <= 0 || b < 0)
+        return ORACLE_ERR;
+    double* x = (double*)malloc(sizeof(double) * (size_t)n_pred * (size_t)H);
+    if (!x)
+        return ORACLE_ERR;
+    const long first_row = (long)b * L + i_first_pred;   /* slot i_first_pred of block b */
+    for (int j = 0; j < n_pred; ++j)
+        load_hidden_row(hidden, hidden_is_f32, first_row + j, H, x + (size_t)j * H);
+
+    int fail = 0;
+#pragma omp parallel
+    {
+        double* w = (double*)malloc(sizeof(double) * (size_t)H);
+#pragma omp for schedule(static)
+        for (long v = 0; v < V; ++v) {
+            if (!w) {
+#pragma omp atomic write
+                fail = 1;
+                continue;
+            }
+            oracle_q4_dequant_row(q4, H, v, w);
+            for (int j = 0; j < n_pred; ++j) {
+                const double* xj = x + (size_t)j * H;
+                double s = 0.0;
+                for (int h = 0; h < H; ++h)
+                    s += xj[h] * w[h];
+                if (bias)
+                    s = s + (double)bias[v];
+                z[(size_t)j * V + v] = s;
+            }
+        }
+        free(w);
+    }
+    free(x);
+    return fail ? ORACLE_ERR : ORACLE_OK;
+}
+
+/* Everything for block b with a q4 head (as oracle_propose_block). */
+int oracle_propose_block_q4(const void* hidden, int hidden_is_f32, const uint8_t* q4,
+                            const float* bias, const uint16_t* w1, const uint16_t* w2,
+                            const uint16_t* conf_w, const int32_t* anchors, int L, int H, int V,
+                            int r, int i_first_pred, int top_k, float p_min, int b, double* z,
+                            int32_t* tokens, int32_t* cand, float* cand_val, float* conf,
+                            int32_t* length)
+{
+    int n_pred = L - i_first_pred;
+    double* zz = z ? z : (double*)malloc(sizeof(double) * (size_t)n_pred * (size_t)V);
+    if (!zz)
+        return ORACLE_ERR;
+    int st = oracle_block_logits_q4(hidden, hidden_is_f32, q4, bias, L, H, V, i_first_pred, b, zz);
+    if (st == ORACLE_OK)
+        st = finish_block(zz, hidden, hidden_is_f32, w1, w2, conf_w, anchors, L, H, V, r,
+                          i_first_pred, top_k, p_min, b, tokens, cand, cand_val, conf, length);
     if (!z)
         free(zz);
     return st;

@@ -10,10 +10,13 @@ from .inputs import (  # noqa: F401
     MASK_TOKEN_ID,
     Config,
     Inputs,
+    Q4Inputs,
     ReducedInputs,
     bf16_bits_to_f32,
     f32_to_bf16_bits,
     make_inputs,
     make_small,
+    q4_blocks,
+    quantize_q4,
     reduce_vocab,
 )

@@ -20,6 +20,15 @@ workloads share identical weights, and the draw order does not matter):
   seeded permutation of range(V) are the reachable rows. Every other row of
   lm_head and markov_w2 is zero and carries an lm_head bias of -1e9; the
   reachable rows carry bias 0. markov_w1 is left untouched.
+* q4 head (``quantize_q4``): the same lm_head requantized to 4-bit blocks of
+  32 weights along H (the block format is described at ``Q4Inputs``). Mode
+  "round": d = binary16(max |w| / 8) per block and code q = clip(rint(w / d)
+  + 8, 0, 15) (code 8 where d = 0), in float64 from the bf16 weights. Mode
+  "random": codes uniform in [0, 16) and d = binary16(N(0, 1/(8 sqrt(H))))
+  from stream("q4", chunk), with every 97th block's scale set to 0, every
+  89th to a subnormal binary16 (2^-20) and every 83rd to its negative. The
+  requantizer is input preparation (the drafter ships already quantized);
+  the proposal step only decodes.
 * confidence trend (``conf_trend``): conf_w is rescaled to norm 0.5 and each
   prediction slot j of every block is shifted along conf_w so that
   conf_w . hidden = logit(p_j) + (conf_w . z), with p_j falling linearly from
@@ -46,6 +55,7 @@ TENSOR_CODE = {
     "conf_w": 5,
     "anchors": 6,
     "reachable": 7,
+    "q4": 8,
 }
 
 ANCHOR_FIRST = "anchor_first"
@@ -302,3 +312,112 @@ def reduce_vocab(inp: Inputs) -> ReducedInputs:
     return ReducedInputs(cfg=inp.cfg, hidden=inp.hidden, lm_head=np.ascontiguousarray(inp.lm_head[d2t]),
                          d2t=d2t, markov_w1=inp.markov_w1, markov_w2=w2, conf_w=inp.conf_w,
                          anchors=inp.anchors)
+
+
+# ---------------------------------------------------------------------------
+# 4-bit head
+# ---------------------------------------------------------------------------
+
+Q4_BLOCK = 32
+Q4_BLOCK_BYTES = 18
+
+
+@dataclass
+class Q4Inputs:
+    """The same draft with lm_head in a 4-bit block format (GGUF's plain
+    4-bit type): each row is H/32 blocks of 18 bytes, a binary16 scale d (low
+    byte first) and 16 code bytes; code byte j holds element j of the block
+    in its low nibble and element j + 16 in its high nibble, and an element
+    with code q is worth d * (q - 8)."""
+    cfg: Config
+    hidden: np.ndarray
+    lm_head_q4: np.ndarray        # uint8 [V, H/32 * 18]
+    lm_head_bias: Optional[np.ndarray]
+    markov_w1: Optional[np.ndarray]
+    markov_w2: Optional[np.ndarray]
+    conf_w: Optional[np.ndarray]
+    anchors: np.ndarray
+    reachable: Optional[np.ndarray] = None
+
+    @property
+    def hidden_f32(self) -> bool:
+        return self.hidden.dtype == np.float32
+
+
+def q4_blocks(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """GGUF 4-bit blocks from codes uint8 [V, H] (values 0..15) and binary16
+    scales [V, H/32]: uint8 [V, H/32 * 18]."""
+    V, H = codes.shape
+    nb = H // Q4_BLOCK
+    c = np.asarray(codes, dtype=np.uint8).reshape(V, nb, Q4_BLOCK)
+    qs = (c[:, :, :16] | (c[:, :, 16:] << 4)).astype(np.uint8)
+    sb = np.ascontiguousarray(np.asarray(scales, dtype=np.float16)).view(np.uint8).reshape(V, nb, 2)
+    return np.ascontiguousarray(np.concatenate([sb, qs], axis=2).reshape(V, nb * Q4_BLOCK_BYTES))
+
+
+def _q4_round_rows(w_bits: np.ndarray) -> np.ndarray:
+    """Round-to-nearest requantization of bf16 rows [n, H] into q4 blocks."""
+    n, H = w_bits.shape
+    w = bf16_bits_to_f32(w_bits).astype(np.float64).reshape(n, H // Q4_BLOCK, Q4_BLOCK)
+    d = (np.abs(w).max(axis=2) / 8.0).astype(np.float16)
+    d64 = d.astype(np.float64)[:, :, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(d64 != 0.0, np.clip(np.rint(w / np.where(d64 != 0.0, d64, 1.0)) + 8, 0, 15), 8)
+    return q4_blocks(q.astype(np.uint8).reshape(n, H), d)
+
+
+def _q4_random_rows(seed: int, chunk: int, n: int, H: int, row0: int) -> np.ndarray:
+    g = _stream(seed, "q4", chunk)
+    nb = H // Q4_BLOCK
+    codes = g.integers(0, 16, size=(n, H), dtype=np.uint8)
+    d = (g.standard_normal((n, nb)) / (8.0 * math.sqrt(H))).astype(np.float16)
+    idx = (row0 + np.arange(n))[:, None] * nb + np.arange(nb)[None, :]
+    d[idx % 83 == 0] = -d[idx % 83 == 0]
+    d[idx % 89 == 0] = np.float16(2.0 ** -20)
+    d[idx % 97 == 0] = np.float16(0.0)
+    return q4_blocks(codes, d)
+
+
+_Q4_CACHE: dict = {}
+
+
+def quantize_q4(inp: Inputs, mode: str = "round") -> Q4Inputs:
+    """``inp`` with its lm_head as q4 blocks (see the module recipe)."""
+    c = inp.cfg
+    if c.H % Q4_BLOCK != 0:
+        raise ValueError("the 4-bit head needs H to be a multiple of 32")
+    key = (c.seed, c.V, c.H, mode, c.reachable, inp.lm_head.ctypes.data if mode == "round" else 0)
+    q4 = _Q4_CACHE.get(key)
+    if q4 is None:
+        V, H = c.V, c.H
+        q4 = np.empty((V, H // Q4_BLOCK * Q4_BLOCK_BYTES), dtype=np.uint8)
+        n_chunks = (V + CHUNK_ROWS - 1) // CHUNK_ROWS
+
+        def fill(ch: int) -> None:
+            r0 = ch * CHUNK_ROWS
+            r1 = min(V, r0 + CHUNK_ROWS)
+            if mode == "round":
+                q4[r0:r1] = _q4_round_rows(inp.lm_head[r0:r1])
+            elif mode == "random":
+                q4[r0:r1] = _q4_random_rows(c.seed, ch, r1 - r0, H, r0)
+            else:
+                raise ValueError(f"unknown q4 mode {mode}")
+
+        if n_chunks == 1:
+            fill(0)
+        else:
+            with ThreadPoolExecutor(_threads()) as ex:
+                list(ex.map(fill, range(n_chunks)))
+        if mode == "random" and inp.reachable is not None:
+            # unreachable rows stay zero weights (scale 0, code 8), as in the bf16 form
+            keep = np.zeros(V, dtype=bool)
+            keep[inp.reachable] = True
+            zero_row = q4_blocks(np.full((1, H), 8, np.uint8), np.zeros((1, H // Q4_BLOCK), np.float16))
+            q4[~keep] = zero_row
+        if q4.nbytes > (256 << 20):
+            for k in [k for k, v in _Q4_CACHE.items() if v.nbytes > (256 << 20)]:
+                del _Q4_CACHE[k]
+        _Q4_CACHE[key] = q4
+    return Q4Inputs(cfg=c, hidden=inp.hidden, lm_head_q4=q4, lm_head_bias=inp.lm_head_bias,
+                    markov_w1=inp.markov_w1, markov_w2=inp.markov_w2, conf_w=inp.conf_w,
+                    anchors=inp.anchors, reachable=inp.reachable)

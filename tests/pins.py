@@ -16,7 +16,8 @@ from dataclasses import replace
 
 import numpy as np
 
-from synthetic import ReducedInputs, bf16_bits_to_f32, f32_to_bf16_bits, make_small, reduce_vocab
+from synthetic import (Q4Inputs, ReducedInputs, bf16_bits_to_f32, f32_to_bf16_bits, make_small,
+                       q4_blocks, quantize_q4, reduce_vocab)
 from synthetic.inputs import BONUS_ANCHOR, Config, Inputs
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -534,6 +535,143 @@ def pin_gated_equals_masked_full_step(orc):
     inp = cases[0]
     lens = [orc.propose_block_gated(inp, b, 0.5, 1, keep_logits=False)["length"] for b in range(4)]
     assert min(lens) < inp.cfg.n_pred
+
+
+# --------------------------------------------------------------------------
+# 4-bit head (GGUF plain 4-bit blocks; the reading is stated in oracle.c)
+# --------------------------------------------------------------------------
+
+def _golden_q4_row():
+    """(row bytes uint8 [72], values float64 [128]) of golden/q4_row_h128.txt."""
+    raw, vals = [], []
+    with open(os.path.join(GOLDEN, "q4_row_h128.txt")) as f:
+        for line in f:
+            t = line.split()
+            if not t or t[0].startswith("#"):
+                continue
+            if t[0] == "bytes":
+                raw += [int(x, 16) for x in t[1:]]
+            elif t[0] == "values":
+                for x in t[1:]:
+                    if "*2^" in x:
+                        k, e = x.split("*2^")
+                        vals.append(math.ldexp(float(k), int(e)))
+                    else:
+                        vals.append(float(x))
+    return np.array(raw, dtype=np.uint8), np.array(vals, dtype=np.float64)
+
+
+def _np_q4_dequant(q4: np.ndarray, H: int) -> np.ndarray:
+    """[V, H] float64 weights of GGUF 4-bit blocks, decoded with numpy's binary16."""
+    V = q4.shape[0]
+    blk = q4.reshape(V, H // 32, 18)
+    d = blk[:, :, :2].copy().view("<f2")[:, :, 0].astype(np.float64)
+    qs = blk[:, :, 2:].astype(np.int64)
+    codes = np.concatenate([qs & 15, qs >> 4], axis=2)        # elements j, then j + 16
+    return (d[:, :, None] * (codes - 8)).reshape(V, H)
+
+
+def _q4_custom(inp: Inputs, q4: np.ndarray) -> Q4Inputs:
+    return Q4Inputs(cfg=inp.cfg, hidden=inp.hidden, lm_head_q4=np.ascontiguousarray(q4),
+                    lm_head_bias=inp.lm_head_bias, markov_w1=inp.markov_w1, markov_w2=inp.markov_w2,
+                    conf_w=inp.conf_w, anchors=inp.anchors, reachable=inp.reachable)
+
+
+def pin_f16_value(orc):
+    """binary16 decoding: hand values and numpy's float16 on all 65536 patterns."""
+    for bits, want in {0x3C00: 1.0, 0xC000: -2.0, 0x7BFF: 65504.0, 0x0001: 2.0 ** -24,
+                       0x0400: 2.0 ** -14, 0x03FF: 1023 * 2.0 ** -24, 0x3555: 0.333251953125,
+                       0xC200: -3.0, 0x8001: -(2.0 ** -24), 0x7C00: math.inf}.items():
+        got = orc.f16_value(bits)
+        assert got == want, f"f16_value({bits:#06x}) = {got!r}, want {want!r}"
+    assert math.copysign(1.0, orc.f16_value(0x8000)) == -1.0
+    allbits = np.arange(1 << 16, dtype=np.uint16)
+    ref = allbits.view(np.float16).astype(np.float64)
+    got = np.array([orc.f16_value(int(b)) for b in allbits])
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all(), allbits[~same][:8]
+
+
+def pin_q4_golden_row(orc):
+    """The hand-decoded row, through the decoder and through the projection
+    (one-hot hidden rows pick the weights out one by one)."""
+    row, want = _golden_q4_row()
+    H = 128
+    assert row.size == H // 32 * 18 and want.size == H
+    got = orc.q4_dequant_row(row.reshape(1, -1), H, 0)
+    assert np.array_equal(got, want), np.nonzero(got != want)
+    # row 1 is row 0 with its blocks in reverse order: the block stride shows
+    q4 = np.stack([row, row.reshape(4, 18)[::-1].ravel()])
+    hidden = np.zeros((1, H, H), dtype=np.uint16)
+    hidden[0, np.arange(H), np.arange(H)] = 0x3F80            # bf16 1.0
+    inp = _custom(1, H, H, 2, 0, hidden, np.zeros((2, H), np.uint16), None, None, [0])
+    z = orc.block_logits(_q4_custom(inp, q4), 0)
+    assert np.array_equal(z[:, 0], want)
+    assert np.array_equal(z[:, 1], want.reshape(4, 32)[::-1].ravel())
+
+
+def pin_q4_logits_vs_numpy(orc):
+    """Random codes and scales (negative, zero and subnormal scales included),
+    fp32 hidden: numpy decode + fp64 matmul."""
+    for layout, f32 in (("anchor_first", True), (BONUS_ANCHOR, False)):
+        inp = make_small(3, 6, 96, 211, 8, top_k=2, layout=layout, hidden_f32=f32, seed=61)
+        q = quantize_q4(inp, "random")
+        w = _np_q4_dequant(q.lm_head_q4, 96)
+        assert np.any(w < 0) and np.any(w == 0)
+        x = (bf16_bits_to_f32(f32_to_bf16_bits(inp.hidden)) if f32 else bf16_bits_to_f32(inp.hidden))
+        x = x.astype(np.float64)[:, inp.cfg.i_first_pred:, :]
+        want = x @ w.T
+        for b in range(inp.cfg.B):
+            z = orc.block_logits(q, b)
+            assert np.allclose(z, want[b], rtol=1e-12, atol=1e-12), np.abs(z - want[b]).max()
+
+
+def pin_q4_equals_bf16_when_weights_are_bf16(orc):
+    """Power-of-two scales make every decoded weight a bf16 value: the q4
+    proposal must then be the bf16 proposal of the decoded head, bit for bit
+    (logits included: the same products summed in the same order)."""
+    inp = make_small(4, 6, 128, 300, 8, top_k=3, conf=True, p_min=0.45, conf_trend=True, seed=62,
+                     w_std=0.5, reachable=120)
+    rng = np.random.default_rng(7)
+    V, H = 300, 128
+    codes = rng.integers(0, 16, size=(V, H), dtype=np.uint8)
+    scales = np.ldexp(1.0, rng.integers(-9, -4, size=(V, H // 32))).astype(np.float16)
+    scales[~np.isin(np.arange(V), inp.reachable)] = 0
+    q4 = q4_blocks(codes, scales)
+    w = _np_q4_dequant(q4, H)
+    lm = f32_to_bf16_bits(w.astype(np.float32))
+    assert np.array_equal(bf16_bits_to_f32(lm).astype(np.float64), w)
+    ref = orc.propose(replace(inp, lm_head=lm))
+    got = orc.propose(_q4_custom(inp, q4))
+    for k in ("logits", "tokens", "candidates", "cand_logits", "conf", "lengths"):
+        assert np.array_equal(got[k], ref[k]), k
+
+
+def pin_q4_scale_linearity(orc):
+    """Doubling every scale doubles every projection exactly (no bias)."""
+    inp = make_small(2, 5, 64, 97, 0, seed=63)
+    q = quantize_q4(inp, "round")
+    q2 = q.lm_head_q4.reshape(97, 2, 18).copy()
+    d = q2[:, :, :2].copy().view("<f2")
+    assert np.all(np.abs(d.astype(np.float64)) < 16000)
+    q2[:, :, :2] = (d * np.float16(2)).view(np.uint8)
+    for b in range(2):
+        z1 = orc.block_logits(q, b)
+        z2 = orc.block_logits(_q4_custom(inp, q2.reshape(97, 36)), b)
+        assert np.array_equal(z2, 2.0 * z1)
+
+
+def pin_q4_zero_weights_give_bias(orc):
+    """Code 8 everywhere (any scale) or scale 0 (any code): the projection is the bias."""
+    inp = make_small(2, 4, 64, 50, 4, reachable=20, seed=64, w_std=0.5)
+    rng = np.random.default_rng(8)
+    eights = q4_blocks(np.full((50, 64), 8, np.uint8),
+                       rng.standard_normal((50, 2)).astype(np.float16))
+    zeros = q4_blocks(rng.integers(0, 16, (50, 64), dtype=np.uint8), np.zeros((50, 2), np.float16))
+    for q4 in (eights, zeros):
+        for b in range(2):
+            z = orc.block_logits(_q4_custom(inp, q4), b)
+            assert np.array_equal(z, np.broadcast_to(inp.lm_head_bias.astype(np.float64), z.shape))
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

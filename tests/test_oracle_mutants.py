@@ -55,6 +55,30 @@ MUTANTS = {
     "gated_keeps_all_candidates": ("                for (int t = 0; t < kb; ++t) {\n                    cand[(size_t)j * top_k + t]",
                                    "                for (int t = 0; t < kb - 1; ++t) {\n                    cand[(size_t)j * top_k + t]"),
     "gated_no_fill": ("            cand_val[(size_t)j * top_k + t] = -INFINITY;", "            cand_val[(size_t)j * top_k + t] = 0.0f;"),
+    "q4_low_nibble_is_high": ("w[i * Q4_BLOCK + j] = d * (double)((int)(qs[j] & 0x0f) - 8);",
+                              "w[i * Q4_BLOCK + j] = d * (double)((int)(qs[j] >> 4) - 8);"),
+    "q4_offset_7": ("w[i * Q4_BLOCK + j + 16] = d * (double)((int)(qs[j] >> 4) - 8);",
+                    "w[i * Q4_BLOCK + j + 16] = d * (double)((int)(qs[j] >> 4) - 7);"),
+    "q4_interleaved_nibbles": (
+        "w[i * Q4_BLOCK + j] = d * (double)((int)(qs[j] & 0x0f) - 8);\n"
+        "            w[i * Q4_BLOCK + j + 16] = d * (double)((int)(qs[j] >> 4) - 8);",
+        "w[i * Q4_BLOCK + 2 * j] = d * (double)((int)(qs[j] & 0x0f) - 8);\n"
+        "            w[i * Q4_BLOCK + 2 * j + 1] = d * (double)((int)(qs[j] >> 4) - 8);"),
+    "q4_scale_big_endian": ("f16_value((uint16_t)(blk[0] | (blk[1] << 8)))",
+                            "f16_value((uint16_t)(blk[1] | (blk[0] << 8)))"),
+    "q4_scale_read_as_bf16": ("const double d = f16_value(", "const double d = bf16_value("),
+    "q4_block_stride_16": ("const uint8_t* blk = row + (long)i * Q4_BLOCK_BYTES;",
+                           "const uint8_t* blk = row + (long)i * 16;"),
+    "q4_row_stride_unpadded": ("const uint8_t* row = q4 + v * (long)nb * Q4_BLOCK_BYTES;",
+                               "const uint8_t* row = q4 + v * (long)nb * 16;"),
+    "f16_subnormal_as_normal": ("v = ldexp((double)f, -24);", "v = ldexp((double)(1024 + f), -25);"),
+    "f16_exponent_bias": ("v = ldexp((double)(1024 + f), e - 25);", "v = ldexp((double)(1024 + f), e - 24);"),
+    "f16_sign_dropped": ("return (bits & 0x8000u) ? -v : v;", "return v;"),
+    "q4_bias_dropped": ("s = s + (double)bias[v];", "s = s + 0.0;"),
+    "q4_bonus_slot_read": ("const long first_row = (long)b * L + i_first_pred;",
+                           "const long first_row = (long)b * L;"),
+    "q4_last_row_skipped": ("for (long v = 0; v < V; ++v) {\n            if (!w) {",
+                            "for (long v = 0; v < V - 1; ++v) {\n            if (!w) {"),
     "hidden_f32_truncated": ("x[h] = bf16_value(oracle_bf16_round(p[h]));",
                              "x[h] = bf16_value((uint16_t)(*(const uint32_t*)&p[h] >> 16));"),
 }
