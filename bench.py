@@ -133,6 +133,9 @@ def main() -> int:
                          "the workload's p_min for every block); value counts submitted slots")
     ap.add_argument("--d2t", action="store_true",
                     help="run the workload's reduced-vocabulary form (dspark_propose_d2t)")
+    ap.add_argument("--q4", action="store_true",
+                    help="run the workload with its lm_head requantized to 4-bit GGUF blocks "
+                         "(dspark_q4_pack once, then dspark_propose_q4 per step)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -155,7 +158,31 @@ def main() -> int:
     inp = make_inputs(cfg)
     log(f"inputs for {cfg.name} generated in {time.perf_counter() - t0:.1f} s")
     stream = torch.cuda.current_stream()
-    if args.d2t:
+    if sum([args.d2t, args.adaptive, args.q4]) > 1:
+        print("--d2t, --adaptive and --q4 are separate forms; pick one", file=sys.stderr)
+        return 2
+    if args.q4:
+        from devutil import to_device_q4
+        from synthetic import quantize_q4
+        if cfg.H % 32 != 0:
+            print(f"--q4 needs H to be a multiple of 32; {cfg.name} has H={cfg.H}", file=sys.stderr)
+            return 2
+        t0 = time.perf_counter()
+        inp = quantize_q4(inp, "round")
+        log(f"lm_head requantized to 4-bit blocks in {time.perf_counter() - t0:.1f} s")
+        d = to_device_q4(inp)
+        del d["lm_head_blocks"]
+        N = cfg.V
+        out = dsp.OutputsQ4(cfg.B, cfg.L, cfg.H, cfg.V, cfg.top_k, cfg.layout, "cuda:0")
+        q4_ws = torch.empty((dsp.q4_workspace_bytes(cfg.B, cfg.L, cfg.H, cfg.V, 1, cfg.layout),),
+                            dtype=torch.uint8, device="cuda:0")
+
+        def step():
+            dsp.propose_q4(d["hidden"], d["lm_head_q4"], d["markov_w1"], d["markov_w2"],
+                           d["anchors"], V=cfg.V, layout=cfg.layout, top_k=cfg.top_k,
+                           p_min=cfg.p_min, lm_head_bias=d["lm_head_bias"], conf_w=d["conf_w"],
+                           out=out, stream=stream)
+    elif args.d2t:
         from devutil import to_device_reduced
         from synthetic import reduce_vocab
         if inp.reachable is None:
@@ -206,9 +233,9 @@ def main() -> int:
         ev.record(stream)   # creates the HIP event before the timed region
         return ev
 
-    plain = not (args.d2t or args.adaptive)
-    # Unmarked steps: the cross-check (and the timed region of the d2t and
-    # adaptive forms, which have no marked entry point).
+    plain = not (args.d2t or args.adaptive or args.q4)
+    # Unmarked steps: the cross-check (and the timed region of the d2t,
+    # adaptive and 4-bit forms, which have no marked entry point).
     ev0, ev1 = event(), event()
     torch.cuda.synchronize()
     w0 = time.perf_counter()
@@ -249,14 +276,19 @@ def main() -> int:
             f"finalize {phases['finalize'] * 1e3:.1f} us")
     else:
         ms = ms_unmarked
-        # the projection alone through dspark_logits (the chain's time is the
-        # step minus it)
+        # the projection alone through dspark_logits / dspark_logits_q4 (the
+        # chain's time is the step minus it)
         evs = [[event() for _ in range(2)] for _ in range(args.steps)]
         for e in evs:
             e[0].record(stream)
-            dsp.logits(d["hidden"], d["lm_head"], layout=cfg.layout,
-                       lm_head_bias=None if args.d2t else d["lm_head_bias"], out=out.logits,
-                       stream=stream)
+            if args.q4:
+                dsp.logits_q4(d["hidden"], d["lm_head_q4"], V=cfg.V, layout=cfg.layout,
+                              lm_head_bias=d["lm_head_bias"], out=out.logits, workspace=q4_ws,
+                              stream=stream)
+            else:
+                dsp.logits(d["hidden"], d["lm_head"], layout=cfg.layout,
+                           lm_head_bias=None if args.d2t else d["lm_head_bias"], out=out.logits,
+                           stream=stream)
             e[1].record(stream)
         torch.cuda.synchronize()
         gemm_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
@@ -287,7 +319,10 @@ def main() -> int:
     M, H, V, r, B, n = cfg.B * cfg.n_pred, cfg.H, N, cfg.r, cfg.B, cfg.n_pred
     flops = 2.0 * M * H * V
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
-    gemm_bytes = V * H * 2 + M * H * 2 + M * V * 4
+    # algorithmic bytes: the head (bf16, or the packed 4-bit head: 4.5 bits per
+    # weight), the hidden rows once, the fp32 logits once
+    head_bytes = dsp.q4_packed_bytes(V, H) if args.q4 else V * H * 2
+    gemm_bytes = head_bytes + M * H * 2 + M * V * 4
     # the projection is matrix-bound above the ridge point (peak FLOP/s over
     # peak bytes/s, 312 FLOP/B), HBM-bound below it
     if flops / gemm_bytes > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
@@ -320,13 +355,16 @@ def main() -> int:
                    "top_k": cfg.top_k, "p_min": cfg.p_min, "layout": cfg.layout,
                    "drafted_tokens_per_step": cfg.drafted_tokens,
                    **({"d2t_draft_vocab": N} if args.d2t else {}),
+                   **({"lm_head": "4-bit GGUF blocks (binary16 scale per 32), packed",
+                       "head_bytes": head_bytes} if args.q4 else {}),
                    **({"adaptive": True, "counted": "submitted slots (sum of lengths)",
                        "submitted_per_step": submitted} if args.adaptive else {})},
         "roofline": {**gemm_roof,
-                     "traffic": None if args.d2t else measured_traffic(cfg.name),
-                     "kernel": "lmhead_gemm", "us": gemm_ms * 1e3,
+                     "traffic": None if (args.d2t or args.q4) else measured_traffic(cfg.name),
+                     "kernel": "q4_prep + lmhead_q4" if args.q4 else "lmhead_gemm",
+                     "us": gemm_ms * 1e3,
                      "timed": "events around the projection inside the timed steps" if plain
-                              else "dspark_logits alone"},
+                              else ("dspark_logits_q4 alone" if args.q4 else "dspark_logits alone")},
         "roofline_chain": {"bound": "hbm", "achieved": chain_gbs, "peak": PEAK_HBM_GBS,
                            "unit": "GB/s", "frac": chain_gbs / PEAK_HBM_GBS,
                            "bytes": chain_bytes, "kernels": "chain_step x n_pred + finalize",

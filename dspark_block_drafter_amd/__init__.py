@@ -40,8 +40,9 @@ MAX_RANK = 256
 
 EXPORTS = ("dspark_workspace_bytes", "dspark_propose", "dspark_propose_marked",
            "dspark_propose_noalloc", "dspark_logits", "dspark_chain",
-           "dspark_propose_d2t", "dspark_propose_adaptive", "dspark_verify", "dspark_read_flags",
-           "dspark_status_string")
+           "dspark_propose_d2t", "dspark_propose_adaptive", "dspark_q4_packed_bytes",
+           "dspark_q4_pack", "dspark_q4_workspace_bytes", "dspark_logits_q4", "dspark_propose_q4",
+           "dspark_verify", "dspark_read_flags", "dspark_status_string")
 
 
 class DsparkError(RuntimeError):
@@ -92,6 +93,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                             _i, _i, _i, _i, _i, _i, _i, _vp, _vp,
                                             _vp, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.dspark_propose_adaptive.restype = _i
+    lib.dspark_q4_packed_bytes.argtypes = [_i, _i]
+    lib.dspark_q4_packed_bytes.restype = _sz
+    lib.dspark_q4_pack.argtypes = [_vp, _i, _i, _vp, _vp]
+    lib.dspark_q4_pack.restype = _i
+    lib.dspark_q4_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
+    lib.dspark_q4_workspace_bytes.restype = _sz
+    lib.dspark_logits_q4.argtypes = [_vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp]
+    lib.dspark_logits_q4.restype = _i
+    lib.dspark_propose_q4.argtypes = lib.dspark_propose.argtypes
+    lib.dspark_propose_q4.restype = _i
     lib.dspark_verify.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp]
     lib.dspark_verify.restype = _i
     lib.dspark_read_flags.argtypes = [_vp, ctypes.POINTER(ctypes.c_uint32), _vp]
@@ -315,6 +326,103 @@ def propose_d2t(hidden, lm_head, d2t, markov_w1, markov_w2, anchors, *, vocab: i
         _ptr(out.conf), _ptr(out.lengths), _stream(hidden, stream))
     if st != OK:
         raise DsparkError(st, "dspark_propose_d2t")
+    return out
+
+
+def q4_packed_bytes(V: int, H: int) -> int:
+    return int(load_library().dspark_q4_packed_bytes(V, H))
+
+
+def q4_workspace_bytes(B: int, L: int, H: int, V: int, top_k: int, layout="anchor_first") -> int:
+    return int(load_library().dspark_q4_workspace_bytes(B, L, H, V, top_k, LAYOUTS[layout]))
+
+
+def q4_pack(blocks, V: int, H: int, *, out=None, stream=None):
+    """Run dspark_q4_pack: ``blocks`` is the device uint8 [V, H/32*18] GGUF 4-bit
+    head; returns the packed head (device uint8, dspark_q4_packed_bytes bytes)."""
+    torch = _torch()
+    lib = load_library()
+    _check_dev("blocks", blocks, torch.uint8, (V, H // 32 * 18))
+    nbytes = q4_packed_bytes(V, H)
+    if nbytes == 0:
+        raise ValueError(f"no 4-bit packing for V={V}, H={H} (H must be a multiple of 32)")
+    if out is None:
+        out = torch.empty((nbytes,), dtype=torch.uint8, device=blocks.device)
+    _check_dev("out", out, torch.uint8, (nbytes,))
+    st = lib.dspark_q4_pack(_ptr(blocks), V, H, _ptr(out), _stream(blocks, stream))
+    if st != OK:
+        raise DsparkError(st, "dspark_q4_pack")
+    return out
+
+
+class OutputsQ4(Outputs):
+    """Outputs of a 4-bit head call: the workspace also holds the per-call
+    preparation of the hidden rows."""
+
+    def __init__(self, B: int, L: int, H: int, V: int, top_k: int, layout, device, **kw):
+        super().__init__(B, L, V, top_k, layout, device, **kw)
+        torch = _torch()
+        nbytes = q4_workspace_bytes(B, L, H, V, top_k, layout)
+        self.workspace = torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=device)
+
+
+def _check_q4_head(lm_head_q4, V, H):
+    torch = _torch()
+    nbytes = q4_packed_bytes(V, H)
+    if nbytes == 0:
+        raise ValueError(f"no 4-bit head for V={V}, H={H} (H must be a multiple of 32)")
+    _check_dev("lm_head_q4", lm_head_q4, torch.uint8, (nbytes,))
+
+
+def propose_q4(hidden, lm_head_q4, markov_w1, markov_w2, anchors, *, V: int,
+               layout="anchor_first", top_k=1, p_min=0.0, lm_head_bias=None, conf_w=None,
+               out: Optional[OutputsQ4] = None, stream=None) -> OutputsQ4:
+    """Run dspark_propose_q4 with a packed 4-bit head (``q4_pack``) of V rows."""
+    torch = _torch()
+    lib = load_library()
+    B, L, H = hidden.shape
+    r = 0 if markov_w1 is None else markov_w1.shape[1]
+    _check_dev("hidden", hidden, hidden.dtype)
+    _check_q4_head(lm_head_q4, V, H)
+    _check_dev("lm_head_bias", lm_head_bias, torch.float32, (V,))
+    _check_dev("markov_w1", markov_w1, torch.bfloat16, (V, r))
+    _check_dev("markov_w2", markov_w2, torch.bfloat16, (V, r))
+    _check_dev("conf_w", conf_w, torch.bfloat16, (H,))
+    _check_dev("anchors", anchors, torch.int32, (B,))
+    if out is None:
+        out = OutputsQ4(B, L, H, V, top_k, layout, hidden.device)
+    st = lib.dspark_propose_q4(
+        _ptr(hidden), _hidden_dtype(hidden), _ptr(lm_head_q4), _ptr(lm_head_bias), _ptr(markov_w1),
+        _ptr(markov_w2), _ptr(conf_w), _ptr(anchors), B, L, H, V, r, LAYOUTS[layout], top_k,
+        float(p_min), _ptr(out.logits), _ptr(out.workspace), out.workspace.numel(),
+        _ptr(out.tokens), _ptr(out.candidates), _ptr(out.cand_logits), _ptr(out.conf),
+        _ptr(out.lengths), _stream(hidden, stream))
+    if st != OK:
+        raise DsparkError(st, "dspark_propose_q4")
+    return out
+
+
+def logits_q4(hidden, lm_head_q4, *, V: int, layout="anchor_first", lm_head_bias=None, out=None,
+              workspace=None, stream=None):
+    """Run dspark_logits_q4 (the 4-bit projection alone); returns fp32 [B*n_pred, V]."""
+    torch = _torch()
+    lib = load_library()
+    B, L, H = hidden.shape
+    _check_dev("hidden", hidden, hidden.dtype)
+    _check_q4_head(lm_head_q4, V, H)
+    _check_dev("lm_head_bias", lm_head_bias, torch.float32, (V,))
+    n = n_pred_of(L, layout)
+    if out is None:
+        out = torch.empty((B * n, V), dtype=torch.float32, device=hidden.device)
+    _check_dev("out", out, torch.float32, (B * n, V))
+    if workspace is None:
+        workspace = torch.empty((q4_workspace_bytes(B, L, H, V, 1, layout),), dtype=torch.uint8,
+                                device=hidden.device)
+    st = lib.dspark_logits_q4(_ptr(hidden), _hidden_dtype(hidden), _ptr(lm_head_q4),
+                              _ptr(lm_head_bias), B, L, H, V, LAYOUTS[layout], _ptr(out),
+                              _ptr(workspace), workspace.numel(), _stream(hidden, stream))
+    if st != OK:
+        raise DsparkError(st, "dspark_logits_q4")
     return out
 
 

@@ -11,7 +11,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libdspark.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["lmhead_gemm.hip", "markov_chain.hip", "lattice_verify.hip", "dspark_api.hip"]
+SOURCES = ["lmhead_gemm.hip", "lmhead_q4.hip", "markov_chain.hip", "lattice_verify.hip",
+           "dspark_api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -26,7 +27,10 @@ FLAGS = [
 # the result, so accumulators in AGPRs cost a copy in and a copy out per tile
 # (chain + finalize 107 -> 101 us per call at the Qwen3-8B shape, 53 -> 51 us
 # at the Gemma shape, identical results).
-SOURCE_FLAGS = {"markov_chain.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# The 4-bit projection scales every MFMA result with VALU FMAs, so it takes
+# the same form (FM = 4: 494 -> 216 registers, occupancy 1 -> 2).
+SOURCE_FLAGS = {"markov_chain.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "lmhead_q4.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

@@ -289,6 +289,45 @@ int propose_impl(const void* hidden, int hidden_dtype, const uint16_t* lm_head,
                      mark_chained);
 }
 
+// Workspace of the 4-bit head: [xp: M x 128 GQ bf16, 256-byte aligned] in
+// front of the chain's workspace.
+size_t q4_prep_bytes(int M, int H) { return align_up((size_t)M * 128 * q4_quads(H) * 2); }
+
+// Checks of the 4-bit projection's own arguments.
+int check_q4(int B, int L, int H, int V, int layout, const void* lm_head_q4) {
+    if (H % kQ4Block != 0) return DSPARK_ERR_UNSUPPORTED;
+    if (!aligned16(lm_head_q4)) return DSPARK_ERR_UNSUPPORTED;
+    const long M = (long)B * (L - first_pred(layout));
+    // per-thread indices of the preparation and the projection fit in 32 bits
+    if (M * 4 * q4_quads(H) > 0x7fffffffL || (long)q4_tiles(V) * q4_quads(H) * 64 > 0x7fffffffL)
+        return DSPARK_ERR_UNSUPPORTED;
+    return DSPARK_OK;
+}
+
+int project_q4(const void* hidden, int hidden_dtype, const void* lm_head_q4, const float* bias,
+               int B, int L, int H, int V, int layout, float* logits, void* workspace,
+               hipStream_t stream) {
+    Q4Args q{};
+    q.i_first = first_pred(layout);
+    q.n_pred = L - q.i_first;
+    q.M = B * q.n_pred;
+    q.hidden = hidden;
+    q.hidden_f32 = hidden_dtype == DSPARK_HIDDEN_F32;
+    q.GQ = q4_quads(H);
+    q.G = H / kQ4Block;
+    q.T16 = q4_tiles(V);
+    q.H = H;
+    q.V = V;
+    q.L = L;
+    char* ws = static_cast<char*>(workspace);
+    q.xp = reinterpret_cast<uint16_t*>(ws);
+    q.packed = static_cast<const uint8_t*>(lm_head_q4);
+    q.bias = bias;
+    q.out = logits;
+    clear_pending_error();
+    return hip_status(launch_lmhead_q4(q, stream));
+}
+
 }  // namespace
 
 // Scratch of dspark_propose_noalloc: the workspace of one call in a
@@ -494,6 +533,84 @@ int dspark_propose_adaptive(const void* hidden, int hidden_dtype, const uint16_t
     if (st != DSPARK_OK) return st;
     return run_chain(c, true, hidden, hidden_dtype, x, conf_w, B, L, H, V, layout, top_k, 0.0f,
                      workspace, tokens, candidates, cand_logits, conf, lengths, s);
+}
+
+size_t dspark_q4_packed_bytes(int V, int H) {
+    if (V <= 0 || H <= 0 || H % kQ4Block != 0) return 0;
+    return q4_packed_bytes(V, H);
+}
+
+int dspark_q4_pack(const void* blocks, int V, int H, void* packed, void* stream) {
+    if (!blocks || !packed || V <= 0 || H <= 0) return DSPARK_ERR_INVALID_ARG;
+    if (H % kQ4Block != 0 || !aligned16(packed)) return DSPARK_ERR_UNSUPPORTED;
+    if ((long)q4_tiles(V) * q4_quads(H) * 64 > 0x7fffffffL) return DSPARK_ERR_UNSUPPORTED;
+    Q4PackArgs a;
+    a.blocks = static_cast<const uint8_t*>(blocks);
+    a.packed = static_cast<uint8_t*>(packed);
+    a.V = V;
+    a.G = H / kQ4Block;
+    a.GQ = q4_quads(H);
+    a.T16 = q4_tiles(V);
+    clear_pending_error();
+    return hip_status(launch_q4_pack(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t dspark_q4_workspace_bytes(int B, int L, int H, int V, int top_k, int layout) {
+    const size_t base = dspark_workspace_bytes(B, L, V, top_k, layout);
+    if (base == 0 || H <= 0 || H % kQ4Block != 0) return 0;
+    return q4_prep_bytes(B * (L - first_pred(layout)), H) + base;
+}
+
+int dspark_logits_q4(const void* hidden, int hidden_dtype, const void* lm_head_q4,
+                     const float* lm_head_bias, int B, int L, int H, int V, int layout,
+                     float* logits, void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_sizes(B, L, H, V, layout, hidden_dtype);
+    if (st != DSPARK_OK) return st;
+    if (!hidden || !lm_head_q4 || !logits) return DSPARK_ERR_INVALID_ARG;
+    st = check_q4(B, L, H, V, layout, lm_head_q4);
+    if (st != DSPARK_OK) return st;
+    if (!aligned16(hidden)) return DSPARK_ERR_UNSUPPORTED;
+    if (!workspace || reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+        return DSPARK_ERR_WORKSPACE;
+    if (workspace_bytes < q4_prep_bytes(B * (L - first_pred(layout)), H)) return DSPARK_ERR_WORKSPACE;
+    return project_q4(hidden, hidden_dtype, lm_head_q4, lm_head_bias, B, L, H, V, layout, logits,
+                      workspace, static_cast<hipStream_t>(stream));
+}
+
+int dspark_propose_q4(const void* hidden, int hidden_dtype, const void* lm_head_q4,
+                      const float* lm_head_bias, const uint16_t* markov_w1,
+                      const uint16_t* markov_w2, const uint16_t* conf_w, const int32_t* anchors,
+                      int B, int L, int H, int V, int r, int layout, int top_k, float p_min,
+                      float* logits, void* workspace, size_t workspace_bytes, int32_t* tokens,
+                      int32_t* candidates, float* cand_logits, float* conf, int32_t* lengths,
+                      void* stream) {
+    int st = check_sizes(B, L, H, V, layout, hidden_dtype);
+    if (st != DSPARK_OK) return st;
+    st = check_chain_args(V, r, top_k, p_min, markov_w1, markov_w2);
+    if (st != DSPARK_OK) return st;
+    if (!hidden || !lm_head_q4 || !logits || !anchors || !tokens || !candidates || !lengths)
+        return DSPARK_ERR_INVALID_ARG;
+    st = check_q4(B, L, H, V, layout, lm_head_q4);
+    if (st != DSPARK_OK) return st;
+    if (!aligned16(hidden) || !aligned16(logits) || (conf_w && !aligned16(conf_w)))
+        return DSPARK_ERR_UNSUPPORTED;
+    if (!workspace || reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+        return DSPARK_ERR_WORKSPACE;
+    if (workspace_bytes < dspark_q4_workspace_bytes(B, L, H, V, top_k, layout))
+        return DSPARK_ERR_WORKSPACE;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int n_pred = L - first_pred(layout);
+    void* chain_ws = static_cast<char*>(workspace) + q4_prep_bytes(B * n_pred, H);
+    // the 4-bit projection leaves no slab maxima: the chain runs unbounded
+    const ChainArgs c = chain_args(logits, markov_w1, markov_w2, ChainExtras(), anchors, B, L, H, V, r,
+                                   layout, top_k, hidden_dtype == DSPARK_HIDDEN_F32, chain_ws, lengths,
+                                   false);
+    st = project_q4(hidden, hidden_dtype, lm_head_q4, lm_head_bias, B, L, H, V, layout, logits,
+                    workspace, s);
+    if (st != DSPARK_OK) return st;
+    return run_chain(c, false, hidden, hidden_dtype, ChainExtras(), conf_w, B, L, H, V, layout, top_k,
+                     p_min, chain_ws, tokens, candidates, cand_logits, conf, lengths, s);
 }
 
 int dspark_verify(const int32_t* candidates, const int32_t* lengths, const int32_t* target, int B,

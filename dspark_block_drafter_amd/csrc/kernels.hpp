@@ -47,6 +47,38 @@ struct GemmArgs {
 };
 hipError_t launch_lmhead_gemm(const GemmArgs& a, bool hidden_f32, hipStream_t stream);
 
+// ---- 4-bit lm_head ------------------------------------------------------------
+// GGUF plain 4-bit blocks (kQ4Block weights: binary16 scale + 16 code bytes)
+// and their packed form: V in tiles of 16 rows, H in quads of 4 blocks, a
+// kQ4CodeRec-byte code record and a kQ4ScaleRec-byte scale record per (tile,
+// quad); all code records first, then all scale records.
+constexpr int kQ4Block = 32, kQ4BlockBytes = 18, kQ4CodeRec = 1024, kQ4ScaleRec = 128;
+inline int q4_tiles(int V) { return (V + 15) / 16; }
+inline int q4_quads(int H) { return (H / kQ4Block + 3) / 4; }
+inline size_t q4_packed_bytes(int V, int H) {
+    return (size_t)q4_tiles(V) * q4_quads(H) * (kQ4CodeRec + kQ4ScaleRec);
+}
+
+struct Q4PackArgs {
+    const uint8_t* blocks;   // [V, G * kQ4BlockBytes]
+    uint8_t* packed;         // q4_packed_bytes(V, H)
+    int V, G, GQ, T16;       // G = H / 32 blocks per row, GQ = q4_quads(H), T16 = q4_tiles(V)
+};
+hipError_t launch_q4_pack(const Q4PackArgs& a, hipStream_t stream);
+
+struct Q4Args {
+    const void* hidden;      // [B, L, H] bf16 bits or fp32
+    int hidden_f32;
+    uint16_t* xp;            // [M, 128 * GQ] bf16 bits: hidden rows, each block in the MFMA's k order
+    const uint8_t* packed;   // the packed head
+    const float* bias;       // [V] or nullptr
+    float* out;              // [M, V]
+    int M, V, H, G, GQ, T16;
+    int L, n_pred, i_first;  // row m reads hidden row (m / n_pred) * L + i_first + m % n_pred
+};
+// The preparation of xp, then the projection.
+hipError_t launch_lmhead_q4(const Q4Args& a, hipStream_t stream);
+
 // ---- Markov chain -----------------------------------------------------------
 // Chain step geometry. With V % 4 == 0 a workgroup streams a contiguous range
 // of tiles of chain_tile(B, r) columns in one of three forms:

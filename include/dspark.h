@@ -106,9 +106,9 @@ typedef enum {
  * Bytes of device workspace that dspark_propose / dspark_chain need for these
  * sizes (pure host function, no HIP call). Returns 0 if the sizes are invalid.
  * The workspace holds the flags word, the per-slot running argmax words and,
- * for top_k > 1, the per-row maximum bins of the projection (which bound the
- * top-k scores and let the chain skip hopeless columns) and the
- * per-workgroup top-k partial lists. Its contents need no initialisation and
+ * for top_k > 1, the per-row slab maxima of the projection and their k-th
+ * largest per row (which bound the top-k scores and let the chain skip
+ * hopeless columns) and the per-workgroup top-k partial lists. Its contents need no initialisation and
  * are overwritten by every call.
  */
 size_t dspark_workspace_bytes(int B, int L, int V, int top_k, int layout);
@@ -294,6 +294,82 @@ int dspark_propose_adaptive(const void* hidden, int hidden_dtype, const uint16_t
                             float* logits, void* workspace, size_t workspace_bytes,
                             int32_t* tokens, int32_t* candidates, float* cand_logits, float* conf,
                             int32_t* lengths, void* stream);
+
+/*
+ * ---- 4-bit lm_head ---------------------------------------------------------
+ * The pages validate the Qwen3.8-27B drafter on the device as a requantized
+ * 4-bit GGUF (lucebox PR #626 "feat(qwen38): add adaptive concurrent DSpark
+ * speculation", Summary -> Drafter) but do not give its block layout. The
+ * reading implemented here is GGUF's plain 4-bit type: each row of lm_head
+ * is H/32 blocks of 18 bytes -- an IEEE binary16 scale d (low byte first)
+ * and 16 code bytes, code byte j giving element j of the block its low
+ * nibble and element j + 16 its high nibble -- and an element with code q is
+ * worth d * (q - 8). The projection is computed over those exact weights;
+ * every other step is dspark_propose's.
+ */
+
+/*
+ * Bytes of the packed form of a 4-bit head with V rows and H columns (pure
+ * host function); 0 if V <= 0, H <= 0 or H is not a multiple of 32.
+ */
+size_t dspark_q4_packed_bytes(int V, int H);
+
+/*
+ * Rearranges a 4-bit head from its GGUF blocks into the packed form the
+ * projection streams (once, when the weights are loaded): rows in tiles of
+ * 16, blocks in quads of 4, code bytes interleaved so that one wave-wide
+ * 16-byte load brings one quad of blocks of one tile; rows past V and blocks
+ * past H/32 are padded with weight 0.
+ *
+ *   blocks   DEVICE uint8 [V, H/32 * 18]: the GGUF blocks, any alignment.
+ *   V, H     rows and columns; H a multiple of 32.
+ *   packed   DEVICE, 16-byte aligned, dspark_q4_packed_bytes(V, H) bytes,
+ *            owned by the caller, fully overwritten.
+ * Returns a dspark_status (DSPARK_ERR_UNSUPPORTED if H % 32 != 0).
+ */
+int dspark_q4_pack(const void* blocks, int V, int H, void* packed, void* stream);
+
+/*
+ * Workspace bytes of dspark_propose_q4 (pure host function; 0 for invalid
+ * sizes): dspark_workspace_bytes(B, L, V, top_k, layout) plus the per-call
+ * preparation of the hidden rows (bf16 rows in the projection's k order and
+ * per-block row sums, about B*n_pred*H*2 bytes). dspark_logits_q4 needs this
+ * with any valid top_k.
+ */
+size_t dspark_q4_workspace_bytes(int B, int L, int H, int V, int top_k, int layout);
+
+/*
+ * Step 1 alone with a 4-bit head: logits[b*n_pred + j][v] = sum_h
+ * hidden[b][i_first_pred + j][h] * w[v][h] (+ lm_head_bias[v]), w the
+ * decoded weights, accumulated in fp32 (each block's partial is scaled by its
+ * d in fp32).
+ *
+ *   lm_head_q4  DEVICE: the head as dspark_q4_pack wrote it for (V, H).
+ *   H           a multiple of 32.
+ *   workspace   DEVICE, 256-byte aligned, dspark_q4_workspace_bytes(B, L, H,
+ *               V, 1, layout) bytes.
+ * Every other argument is as in dspark_logits. Returns a dspark_status.
+ */
+int dspark_logits_q4(const void* hidden, int hidden_dtype, const void* lm_head_q4,
+                     const float* lm_head_bias, int B, int L, int H, int V, int layout,
+                     float* logits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The whole proposal step with a 4-bit head: dspark_logits_q4, then steps 2-4
+ * exactly as dspark_propose runs them on those projections.
+ *
+ *   lm_head_q4  DEVICE: as dspark_q4_pack wrote it for (V, H); H % 32 == 0.
+ *   workspace   DEVICE, 256-byte aligned, at least
+ *               dspark_q4_workspace_bytes(B, L, H, V, top_k, layout) bytes.
+ * Every other argument is as in dspark_propose. Returns a dspark_status.
+ */
+int dspark_propose_q4(const void* hidden, int hidden_dtype, const void* lm_head_q4,
+                      const float* lm_head_bias, const uint16_t* markov_w1,
+                      const uint16_t* markov_w2, const uint16_t* conf_w, const int32_t* anchors,
+                      int B, int L, int H, int V, int r, int layout, int top_k, float p_min,
+                      float* logits, void* workspace, size_t workspace_bytes, int32_t* tokens,
+                      int32_t* candidates, float* cand_logits, float* conf, int32_t* lengths,
+                      void* stream);
 
 /*
  * Greedy verification of a proposal against the target's tokens: the target

@@ -18,7 +18,7 @@ def to_device(inp, device="cuda:0") -> dict:
     hidden = f32(inp.hidden) if inp.hidden_f32 else bf16(inp.hidden)
     return {
         "hidden": hidden,
-        "lm_head": bf16(inp.lm_head),
+        "lm_head": bf16(getattr(inp, "lm_head", None)),
         "lm_head_bias": f32(inp.lm_head_bias),
         "markov_w1": bf16(inp.markov_w1),
         "markov_w2": bf16(inp.markov_w2),
@@ -85,3 +85,28 @@ def scatter_logits(logits_d: np.ndarray, d2t: np.ndarray, V: int) -> np.ndarray:
     full = np.full((logits_d.shape[0], V), np.float32(-1e9), dtype=np.float32)
     full[:, d2t] = logits_d
     return full
+
+
+def to_device_q4(qinp, device="cuda:0") -> dict:
+    """Device tensors of a 4-bit-head input (synthetic.Q4Inputs); the head is
+    uploaded as its GGUF blocks and packed on the device."""
+    import torch
+    import dspark_block_drafter_amd as dsp
+    d = to_device(qinp, device)
+    c = qinp.cfg
+    blocks = torch.from_numpy(np.ascontiguousarray(qinp.lm_head_q4)).to(device)
+    d["lm_head_blocks"] = blocks
+    d["lm_head_q4"] = dsp.q4_pack(blocks, c.V, c.H)
+    return d
+
+
+def run_propose_q4(qinp, dev=None, out=None):
+    import dspark_block_drafter_amd as dsp
+    import torch
+    d = dev if dev is not None else to_device_q4(qinp)
+    c = qinp.cfg
+    res = dsp.propose_q4(d["hidden"], d["lm_head_q4"], d["markov_w1"], d["markov_w2"], d["anchors"],
+                         V=c.V, layout=c.layout, top_k=c.top_k, p_min=c.p_min,
+                         lm_head_bias=d["lm_head_bias"], conf_w=d["conf_w"], out=out)
+    torch.cuda.synchronize()
+    return res

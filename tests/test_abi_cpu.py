@@ -200,3 +200,60 @@ def test_noalloc_validates_before_anything(lib):
     assert call(B=512, L=64, V=248320, top_k=4) == dsp.ERR_SCRATCH
     assert dsp.workspace_bytes(512, 64, 248320, 4) > dsp.NOALLOC_SCRATCH_BYTES
     assert "static scratch" in dsp.status_string(dsp.ERR_SCRATCH)
+
+
+def test_q4_sizes(lib):
+    """Packed 4-bit head: (ceil(V/16) tiles) x (ceil(H/128) quads) x (1024 + 128) bytes;
+    the 4-bit workspace adds M x 128 ceil(H/128) bf16 (256-aligned) in front of
+    the chain's."""
+    def al(x):
+        return (x + 255) // 256 * 256
+    for V, H in [(512, 64), (151936, 4096), (248320, 5120), (262144, 2816), (37, 96)]:
+        assert lib.dspark_q4_packed_bytes(V, H) == (V + 15) // 16 * ((H // 32 + 3) // 4) * 1152
+    for V, H in [(0, 64), (10, 0), (10, 48), (10, -32)]:
+        assert lib.dspark_q4_packed_bytes(V, H) == 0
+    for B, L, H, V, k, lay in [(64, 16, 5120, 248320, 4, 0), (4, 7, 2816, 262144, 1, 1), (1, 4, 64, 512, 1, 0)]:
+        M = B * (L - lay)
+        assert lib.dspark_q4_workspace_bytes(B, L, H, V, k, lay) == (
+            al(M * 128 * ((H // 32 + 3) // 4) * 2) + lib.dspark_workspace_bytes(B, L, V, k, lay))
+    assert lib.dspark_q4_workspace_bytes(2, 4, 48, 512, 1, 0) == 0
+    assert lib.dspark_q4_workspace_bytes(2, 4, 64, 512, 17, 0) == 0
+
+
+def propose_q4(lib, **kw):
+    a = dict(hidden=P, hidden_dtype=0, lm_head=P, bias=None, w1=P, w2=P, conf_w=P, anchors=P,
+             B=2, L=4, H=64, V=512, r=8, layout=0, top_k=2, p_min=0.5, logits=P, ws=P,
+             ws_bytes=1 << 30, tokens=P, cand=P, cand_logits=P, conf=P, lengths=P, stream=None)
+    a.update(kw)
+    return lib.dspark_propose_q4(a["hidden"], a["hidden_dtype"], a["lm_head"], a["bias"], a["w1"],
+                                 a["w2"], a["conf_w"], a["anchors"], a["B"], a["L"], a["H"], a["V"],
+                                 a["r"], a["layout"], a["top_k"], ctypes.c_float(a["p_min"]),
+                                 a["logits"], a["ws"], a["ws_bytes"], a["tokens"], a["cand"],
+                                 a["cand_logits"], a["conf"], a["lengths"], a["stream"])
+
+
+@pytest.mark.parametrize("kw", INVALID, ids=[",".join(f"{k}={v}" for k, v in d.items()) for d in INVALID])
+def test_propose_q4_rejects_invalid(lib, kw):
+    assert propose_q4(lib, **kw) == dsp.ERR_INVALID_ARG
+
+
+def test_q4_rejects_unsupported_and_workspace(lib):
+    assert propose_q4(lib, H=48) == dsp.ERR_UNSUPPORTED           # not a multiple of 32
+    assert propose_q4(lib, lm_head=P + 8) == dsp.ERR_UNSUPPORTED  # packed head misaligned
+    assert propose_q4(lib, hidden=P + 4) == dsp.ERR_UNSUPPORTED
+    need = lib.dspark_q4_workspace_bytes(2, 4, 64, 512, 2, 0)
+    assert propose_q4(lib, ws_bytes=need - 1) == dsp.ERR_WORKSPACE
+    assert propose_q4(lib, ws=None) == dsp.ERR_WORKSPACE
+    assert propose_q4(lib, ws=P + 64) == dsp.ERR_WORKSPACE
+    # the bf16 workspace alone is not enough for the 4-bit call
+    assert propose_q4(lib, ws_bytes=lib.dspark_workspace_bytes(2, 4, 512, 2, 0)) == dsp.ERR_WORKSPACE
+    lq = lib.dspark_logits_q4
+    assert lq(P, 0, P, None, 0, 4, 64, 512, 0, P, P, 1 << 30, None) == dsp.ERR_INVALID_ARG
+    assert lq(None, 0, P, None, 2, 4, 64, 512, 0, P, P, 1 << 30, None) == dsp.ERR_INVALID_ARG
+    assert lq(P, 0, P, None, 2, 4, 48, 512, 0, P, P, 1 << 30, None) == dsp.ERR_UNSUPPORTED
+    assert lq(P, 0, P, None, 2, 4, 64, 512, 0, P, P, 16, None) == dsp.ERR_WORKSPACE
+    pk = lib.dspark_q4_pack
+    assert pk(None, 512, 64, P, None) == dsp.ERR_INVALID_ARG
+    assert pk(P, 0, 64, P, None) == dsp.ERR_INVALID_ARG
+    assert pk(P, 512, 48, P, None) == dsp.ERR_UNSUPPORTED
+    assert pk(P, 512, 64, P + 4, None) == dsp.ERR_UNSUPPORTED
