@@ -289,8 +289,9 @@ int propose_impl(const void* hidden, int hidden_dtype, const uint16_t* lm_head,
                      mark_chained);
 }
 
-// Workspace of the 4-bit head: [xp: M x 128 GQ bf16, 256-byte aligned] in
-// front of the chain's workspace.
+// Preparation area of the 4-bit projection: xp, M x 128 GQ bf16, 256-byte
+// aligned. dspark_propose_q4 places it after the chain's workspace (so the
+// flags word stays at offset 0); dspark_logits_q4 uses it from offset 0.
 size_t q4_prep_bytes(int M, int H) { return align_up((size_t)M * 128 * q4_quads(H) * 2); }
 
 // Checks of the 4-bit projection's own arguments.
@@ -305,7 +306,7 @@ int check_q4(int B, int L, int H, int V, int layout, const void* lm_head_q4) {
 }
 
 int project_q4(const void* hidden, int hidden_dtype, const void* lm_head_q4, const float* bias,
-               int B, int L, int H, int V, int layout, float* logits, void* workspace,
+               int B, int L, int H, int V, int layout, float* logits, void* prep,
                hipStream_t stream) {
     Q4Args q{};
     q.i_first = first_pred(layout);
@@ -319,8 +320,7 @@ int project_q4(const void* hidden, int hidden_dtype, const void* lm_head_q4, con
     q.H = H;
     q.V = V;
     q.L = L;
-    char* ws = static_cast<char*>(workspace);
-    q.xp = reinterpret_cast<uint16_t*>(ws);
+    q.xp = static_cast<uint16_t*>(prep);
     q.packed = static_cast<const uint8_t*>(lm_head_q4);
     q.bias = bias;
     q.out = logits;
@@ -600,17 +600,16 @@ int dspark_propose_q4(const void* hidden, int hidden_dtype, const void* lm_head_
         return DSPARK_ERR_WORKSPACE;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const int n_pred = L - first_pred(layout);
-    void* chain_ws = static_cast<char*>(workspace) + q4_prep_bytes(B * n_pred, H);
+    // [chain workspace][preparation]: the flags word stays at offset 0
+    void* prep = static_cast<char*>(workspace) + dspark_workspace_bytes(B, L, V, top_k, layout);
     // the 4-bit projection leaves no slab maxima: the chain runs unbounded
     const ChainArgs c = chain_args(logits, markov_w1, markov_w2, ChainExtras(), anchors, B, L, H, V, r,
-                                   layout, top_k, hidden_dtype == DSPARK_HIDDEN_F32, chain_ws, lengths,
+                                   layout, top_k, hidden_dtype == DSPARK_HIDDEN_F32, workspace, lengths,
                                    false);
-    st = project_q4(hidden, hidden_dtype, lm_head_q4, lm_head_bias, B, L, H, V, layout, logits,
-                    workspace, s);
+    st = project_q4(hidden, hidden_dtype, lm_head_q4, lm_head_bias, B, L, H, V, layout, logits, prep, s);
     if (st != DSPARK_OK) return st;
     return run_chain(c, false, hidden, hidden_dtype, ChainExtras(), conf_w, B, L, H, V, layout, top_k,
-                     p_min, chain_ws, tokens, candidates, cand_logits, conf, lengths, s);
+                     p_min, workspace, tokens, candidates, cand_logits, conf, lengths, s);
 }
 
 int dspark_verify(const int32_t* candidates, const int32_t* lengths, const int32_t* target, int B,

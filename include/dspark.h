@@ -331,10 +331,11 @@ int dspark_q4_pack(const void* blocks, int V, int H, void* packed, void* stream)
 
 /*
  * Workspace bytes of dspark_propose_q4 (pure host function; 0 for invalid
- * sizes): dspark_workspace_bytes(B, L, V, top_k, layout) plus the per-call
- * preparation of the hidden rows (bf16 rows in the projection's k order and
- * per-block row sums, about B*n_pred*H*2 bytes). dspark_logits_q4 needs this
- * with any valid top_k.
+ * sizes): dspark_workspace_bytes(B, L, V, top_k, layout) for the chain, at
+ * offset 0 (dspark_read_flags reads it as for dspark_propose), followed by the
+ * per-call preparation of the hidden rows (bf16 rows in the projection's k
+ * order, B*n_pred*128*ceil(H/128)*2 bytes rounded up to 256).
+ * dspark_logits_q4 needs this with any valid top_k.
  */
 size_t dspark_q4_workspace_bytes(int B, int L, int H, int V, int top_k, int layout);
 
@@ -400,7 +401,8 @@ int dspark_verify(const int32_t* candidates, const int32_t* lengths, const int32
 
 /*
  * Copies the flags word of `workspace` (written by the last dspark_propose /
- * dspark_propose_d2t / dspark_chain on it) to *flags after `stream` has drained; this call does
+ * dspark_propose_d2t / dspark_propose_adaptive / dspark_propose_q4 /
+ * dspark_chain on it) to *flags after `stream` has drained; this call does
  * synchronise the stream. Returns a dspark_status.
  */
 int dspark_read_flags(const void* workspace, uint32_t* flags, void* stream);

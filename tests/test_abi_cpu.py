@@ -204,8 +204,8 @@ def test_noalloc_validates_before_anything(lib):
 
 def test_q4_sizes(lib):
     """Packed 4-bit head: (ceil(V/16) tiles) x (ceil(H/128) quads) x (1024 + 128) bytes;
-    the 4-bit workspace adds M x 128 ceil(H/128) bf16 (256-aligned) in front of
-    the chain's."""
+    the 4-bit workspace adds M x 128 ceil(H/128) bf16 (256-aligned) after the
+    chain's."""
     def al(x):
         return (x + 255) // 256 * 256
     for V, H in [(512, 64), (151936, 4096), (248320, 5120), (262144, 2816), (37, 96)]:

@@ -180,3 +180,18 @@ def test_propose_q4_full_size(dev, orc, name):
     assert np.array_equal(g["candidates"][:, :, 0], g["tokens"])
     if q.reachable is not None:
         assert np.all(np.isin(g["candidates"], q.reachable))
+
+
+def test_q4_flags_in_the_workspace(dev):
+    """The chain's flags word sits at offset 0 of the 4-bit call's workspace:
+    clear after a valid call, DSPARK_FLAG_BAD_ANCHOR after an anchor outside
+    [0, V) (which the kernels replace by 0)."""
+    import dspark_block_drafter_amd as dsp
+    from devutil import run_propose_q4, to_device_q4
+    q = quantize_q4(make_small(3, 4, 64, 700, 8, top_k=2, seed=84), "random")
+    d = to_device_q4(q)
+    out = run_propose_q4(q, dev=d)
+    assert dsp.read_flags(out) == 0
+    d["anchors"][1] = 100000
+    out = run_propose_q4(q, dev=d, out=out)
+    assert dsp.read_flags(out) & dsp.FLAG_BAD_ANCHOR
