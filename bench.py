@@ -39,8 +39,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # reported for any other source or workload.
 GEMM_TRAFFIC = {
     "workload": "qwen38_27b_throughput",
-    "source_sha256": "9a6f3f13ff5256ed76b086a2566776f659b28fa6246ceb8e1eaf73f0ce808bfc",
-    "bytes": 5607210342,
+    "source_sha256": "39ec223a819fd624bfea00c7382fb0bfa346c6b2433795d10aba7eb66bff476f",
+    "bytes": 5689567312,
 }
 
 
