@@ -14,7 +14,9 @@ import os
 from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libdspark.so")
+# DSPARK_LIBRARY names another build of the library (the test suite's
+# sanitizer build); by default the one built in the package directory.
+LIB_PATH = os.environ.get("DSPARK_LIBRARY") or os.path.join(HERE, "libdspark.so")
 
 ANCHOR_FIRST = 0
 BONUS_ANCHOR = 1

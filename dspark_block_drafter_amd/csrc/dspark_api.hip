@@ -641,6 +641,51 @@ int dspark_read_flags(const void* workspace, uint32_t* flags, void* stream) {
     return hip_status(hipStreamSynchronize(s));
 }
 
+// Dispatch check (host only: no HIP call, no GPU needed; not part of the
+// public header). For every combination of the listed B, V and r, every
+// top_k in 1..DSPARK_MAX_TOP_K and both chain modes (with and without the
+// projection's bound) that dspark_propose's argument checks accept, the chain
+// launcher must reach a compiled kernel with a non-empty grid. Returns the
+// number of combinations that do not (the first is written to first_bad[0..4]
+// = (B, V, r, top_k, bounded)) and the number checked to *checked.
+long dspark_internal_chain_dispatch_walk(const int* Bs, int nB, const int* Vs, int nV, const int* rs,
+                                         int nr, int* first_bad, long* checked) {
+    if (!Bs || !Vs || !rs || !first_bad || !checked || nB < 0 || nV < 0 || nr < 0) return -1;
+    *checked = 0;
+    // stand-in addresses: aligned, non-null, never dereferenced
+    char* const fake = reinterpret_cast<char*>(uintptr_t(1) << 20);
+    const uint16_t* w = reinterpret_cast<const uint16_t*>(fake);
+    const int L = 4, H = 64;
+    long bad = 0;
+    set_chain_dry_dispatch(true);
+    for (int ib = 0; ib < nB; ++ib)
+        for (int iv = 0; iv < nV; ++iv)
+            for (int ir = 0; ir < nr; ++ir)
+                for (int k = 1; k <= DSPARK_MAX_TOP_K; ++k)
+                    for (int bounded = 0; bounded < 2; ++bounded) {
+                        const int B = Bs[ib], V = Vs[iv], r = rs[ir];
+                        const uint16_t* w1 = r > 0 ? w : nullptr;
+                        if (check_sizes(B, L, H, V, DSPARK_LAYOUT_ANCHOR_FIRST, DSPARK_HIDDEN_BF16) != DSPARK_OK ||
+                            check_chain_args(V, r, k, 0.0f, w1, w1) != DSPARK_OK)
+                            continue;
+                        const ChainArgs c = chain_args(reinterpret_cast<const float*>(fake), w1, w1,
+                                                       ChainExtras(), reinterpret_cast<const int32_t*>(fake),
+                                                       B, L, H, V, r, DSPARK_LAYOUT_ANCHOR_FIRST, k, false,
+                                                       fake, reinterpret_cast<int32_t*>(fake), bounded != 0);
+                        ++*checked;
+                        const bool ok = c.nwg >= 1 && launch_chain_step(c, 0, nullptr) == hipSuccess;
+                        if (!ok && bad++ == 0) {
+                            first_bad[0] = B;
+                            first_bad[1] = V;
+                            first_bad[2] = r;
+                            first_bad[3] = k;
+                            first_bad[4] = bounded;
+                        }
+                    }
+    set_chain_dry_dispatch(false);
+    return bad;
+}
+
 const char* dspark_status_string(int status) {
     switch (status) {
         case DSPARK_OK: return "ok";

@@ -217,6 +217,10 @@ hipError_t launch_row_kth(const ChainArgs& a, hipStream_t stream);
 // present) and presets lengths to n_pred; enqueued before the projection.
 hipError_t launch_chain_init(const ChainArgs& a, hipStream_t stream);
 hipError_t launch_chain_step(const ChainArgs& a, int j, hipStream_t stream);
+// While on (on the calling host thread), launch_chain_step selects its kernel
+// as for a launch, launches nothing and returns hipSuccess; a size for which
+// no compiled kernel exists still returns hipErrorInvalidValue.
+void set_chain_dry_dispatch(bool on);
 
 struct FinalArgs {
     const unsigned long long* winners;   // as in ChainArgs

@@ -48,11 +48,13 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 // i = 0..3.
 
 // Four code bytes c0..c3 -> eight bf16 values 128 + nibble, in the k order
-// c0.lo, c2.lo, c1.lo, c3.lo, c0.hi, c2.hi, c1.hi, c3.hi.
-__device__ __forceinline__ u32x4 q4_operand(uint32_t w) {
-    constexpr uint32_t kMask = 0x000F000Fu, kExp = 0x43004300u;   // bf16 128.0 in both halves
-    return u32x4{(w & kMask) | kExp, ((w >> 8) & kMask) | kExp, ((w >> 4) & kMask) | kExp,
-                 ((w >> 12) & kMask) | kExp};
+// c0.lo, c2.lo, c1.lo, c3.lo, c0.hi, c2.hi, c1.hi, c3.hi. The constants
+// kmask = 0x000F000F and kexp = 0x43004300 (bf16 128.0 in both halves) come
+// in registers, so that each pair of codes costs one v_and_or_b32 (a 32-bit
+// literal cannot go into a three-operand instruction).
+__device__ __forceinline__ u32x4 q4_operand(uint32_t w, uint32_t kmask, uint32_t kexp) {
+    return u32x4{(w & kmask) | kexp, ((w >> 8) & kmask) | kexp, ((w >> 4) & kmask) | kexp,
+                 ((w >> 12) & kmask) | kexp};
 }
 
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t bits) {
@@ -240,9 +242,7 @@ __global__ __launch_bounds__(256) void lmhead_q4(Q4Args a) {
     const u32x4 neg136 = u32x4{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u};
     const f32x4 zero4 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // The dequantization constants live in registers, so that each pair of
-    // codes costs one v_and_or_b32 (a 32-bit literal cannot go into a
-    // three-operand instruction).
+    // the decoding constants of q4_operand, held in registers
     uint32_t kmask = 0x000F000Fu, kexp = 0x43004300u;
     asm volatile("" : "+v"(kmask), "+v"(kexp));
 
@@ -270,9 +270,7 @@ __global__ __launch_bounds__(256) void lmhead_q4(Q4Args a) {
             u32x4 bq[CTW];
 #pragma unroll
             for (int j = 0; j < CTW; ++j) {
-                const uint32_t w = code[j][gg];
-                bq[j] = u32x4{(w & kmask) | kexp, ((w >> 8) & kmask) | kexp, ((w >> 4) & kmask) | kexp,
-                              ((w >> 12) & kmask) | kexp};
+                bq[j] = q4_operand(code[j][gg], kmask, kexp);
                 const uint32_t pair = gg < 2 ? sc[j].x : sc[j].y;
                 d[j] = f16_bits_to_f32((gg & 1) ? (pair >> 16) : (pair & 0xffffu));
             }

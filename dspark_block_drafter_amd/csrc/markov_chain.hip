@@ -1593,24 +1593,32 @@ __global__ __launch_bounds__(256) void gate_stop(const int32_t* lengths, int B, 
     }
 }
 
+// Dispatch check: while set (on the calling host thread) launch_chain_step
+// selects its kernel exactly as for a launch and then launches nothing.
+thread_local bool g_dry_dispatch = false;
+
+// The status of a launch that the selection reached.
+inline hipError_t launched() { return g_dry_dispatch ? hipSuccess : hipGetLastError(); }
+
 template <int NB, int KL>
 hipError_t step_direct(const ChainArgs& a, int j, dim3 grid, hipStream_t s) {
     const int rs = (a.r + 15) / 16;
-#define DSPARK_STEP(RSV) hipLaunchKernelGGL((chain_step_direct<NB, KL, RSV>), grid, dim3(256), 0, s, a, j);
+#define DSPARK_STEP(RSV) \
+    if (!g_dry_dispatch) hipLaunchKernelGGL((chain_step_direct<NB, KL, RSV>), grid, dim3(256), 0, s, a, j);
     if (rs <= 1) { DSPARK_STEP(1) }
     else if (rs <= 2) { DSPARK_STEP(2) }
     else if (rs <= 4) { DSPARK_STEP(4) }
     else if (rs <= 8) { DSPARK_STEP(8) }
     else { DSPARK_STEP(16) }
 #undef DSPARK_STEP
-    return hipGetLastError();
+    return launched();
 }
 
 template <int NB, int KL>
 hipError_t step_pipe(const ChainArgs& a, int j, dim3 grid, bool two, hipStream_t s) {
     const int rs = (a.r + 15) / 16;
 #define DSPARK_STEP(RSV, NSV, VWV) \
-    hipLaunchKernelGGL((chain_step_pipe<NB, KL, RSV, NSV, VWV>), grid, dim3(256), 0, s, a, j);
+    if (!g_dry_dispatch) hipLaunchKernelGGL((chain_step_pipe<NB, KL, RSV, NSV, VWV>), grid, dim3(256), 0, s, a, j);
     // Two stages and two workgroups per CU (kChainPipeTwo: top-k lists over
     // two block groups, rank up to 128); three stages, one workgroup per CU,
     // for the widest rank (kChainPipeDeep).
@@ -1629,7 +1637,7 @@ hipError_t step_pipe(const ChainArgs& a, int j, dim3 grid, bool two, hipStream_t
         else return hipErrorInvalidValue;   // narrower ranks take the other forms
     }
 #undef DSPARK_STEP
-    return hipGetLastError();
+    return launched();
 }
 
 // Per-wave rings: as many stages as fit the workgroup's share of the CU's
@@ -1645,8 +1653,9 @@ hipError_t step_wave_rows(const ChainArgs& a, int j, dim3 grid, hipStream_t s) {
     const int rs = chain_wave_rank(a.r);
     const bool two = chain_wave_per_cu(a.B, a.r, a.top_k) == 2;
 #define DSPARK_STEP(RSV, WPCV)                                                                 \
-    hipLaunchKernelGGL((chain_step_wave<NB, KL, RSV, chain_wave_stages<RSV, LROWS, WPCV>(), LROWS>), \
-                       grid, dim3(256), 0, s, a, j);
+    if (!g_dry_dispatch)                                                                       \
+        hipLaunchKernelGGL((chain_step_wave<NB, KL, RSV, chain_wave_stages<RSV, LROWS, WPCV>(), LROWS>), \
+                           grid, dim3(256), 0, s, a, j);
 #define DSPARK_RANK(RSV)                                                                     \
     if constexpr (LROWS < 32 && chain_wave_stages<RSV, LROWS, 2>() >= 2) {                   \
         if (two) { DSPARK_STEP(RSV, 2) }                                                     \
@@ -1661,7 +1670,7 @@ hipError_t step_wave_rows(const ChainArgs& a, int j, dim3 grid, hipStream_t s) {
     else return hipErrorInvalidValue;   // chain_form never picks this form for a wider rank
 #undef DSPARK_RANK
 #undef DSPARK_STEP
-    return hipGetLastError();
+    return launched();
 }
 
 // Pruned form: as many stages as fit its budgets (chain_sparse_per_cu), at most 8.
@@ -1676,8 +1685,9 @@ hipError_t step_sparse_rows(const ChainArgs& a, int j, dim3 grid, hipStream_t s)
     const int rs = chain_wave_rank(a.r);
     const bool two = chain_sparse_per_cu(a.B, a.r, a.top_k) == 2;
 #define DSPARK_STEP(RSV, WPCV)                                                                     \
-    hipLaunchKernelGGL((chain_step_sparse<NB, KL, RSV, chain_sparse_stages<RSV, LROWS, WPCV>(), LROWS>), \
-                       grid, dim3(256), 0, s, a, j);
+    if (!g_dry_dispatch)                                                                           \
+        hipLaunchKernelGGL((chain_step_sparse<NB, KL, RSV, chain_sparse_stages<RSV, LROWS, WPCV>(), LROWS>), \
+                           grid, dim3(256), 0, s, a, j);
 #define DSPARK_RANK(RSV)                                                                         \
     if constexpr (LROWS < 32 && chain_sparse_stages<RSV, LROWS, 2>() >= 2) {                     \
         if (two) { DSPARK_STEP(RSV, 2) }                                                         \
@@ -1692,7 +1702,7 @@ hipError_t step_sparse_rows(const ChainArgs& a, int j, dim3 grid, hipStream_t s)
     else return hipErrorInvalidValue;   // chain_sparse excludes wider ranks
 #undef DSPARK_RANK
 #undef DSPARK_STEP
-    return hipGetLastError();
+    return launched();
 }
 
 template <int NB, int KL>
@@ -1761,6 +1771,8 @@ hipError_t launch_row_kth(const ChainArgs& a, hipStream_t stream) {
     else hipLaunchKernelGGL(row_kth<16>, grid, block, 0, stream, a.smax, nslab, a.kth);
     return hipGetLastError();
 }
+
+void set_chain_dry_dispatch(bool on) { g_dry_dispatch = on; }
 
 hipError_t launch_chain_step(const ChainArgs& a, int j, hipStream_t stream) {
     // Blocks are taken 64 at a time (two 32-wide MFMA column groups) so that a

@@ -104,9 +104,15 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load liboracle.so, compiling it first if it is missing or older than its source."""
+    """Load liboracle.so, compiling it first if it is missing or older than its source.
+    With DSPARK_ORACLE_LIB set, the default library is that prebuilt file
+    instead (the test suite's sanitizer build)."""
     global _LIB
     if path == LIB_PATH and _LIB is not None:
+        return _LIB
+    override = os.environ.get("DSPARK_ORACLE_LIB")
+    if path == LIB_PATH and override:
+        _LIB = _declare(ctypes.CDLL(override))
         return _LIB
     if path == LIB_PATH and (not os.path.exists(path)
                              or os.path.getmtime(path) < os.path.getmtime(SRC_PATH)):

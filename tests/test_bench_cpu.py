@@ -30,7 +30,8 @@ def test_stored_traffic_matches_its_profile():
     text = open(PROFILE).read()
     sha = re.search(r"lmhead_gemm\.hip SHA-256 at measurement: ([0-9a-f]{64})", text).group(1)
     assert sha == bench.GEMM_TRAFFIC["source_sha256"]
-    m = re.search(r"lm_head GEMM per launch: ([0-9.]+) GB read \+ ([0-9.]+) GB written = ([0-9.]+) GB", text)
+    m = re.search(r"lm_head GEMM [^\n]*?per launch: ([0-9.]+) GB read (?:\([^)]*\) )?\+ ([0-9.]+) GB "
+                  r"written = ([0-9.]+) GB", text)
     rd, wr, tot = (float(x) for x in m.groups())
     assert abs(rd + wr - tot) < 0.002
     assert abs(bench.GEMM_TRAFFIC["bytes"] / 1e9 - tot) < 0.001
