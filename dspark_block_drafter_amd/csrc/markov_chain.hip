@@ -32,6 +32,9 @@ namespace dspark {
 namespace {
 
 constexpr int kWaves = 4;
+// finalize runs one wave per (block, slot) from this many pairs on, one
+// workgroup per pair below it.
+constexpr long kFinalWavePairs = 512;
 static_assert(kChainTileV == kWaves * 32, "one 32-column block per wave");
 
 __global__ __launch_bounds__(256) void chain_init(u64* winners, int n, uint32_t* flags,
@@ -1474,13 +1477,23 @@ __device__ __forceinline__ int final_token(const FinalArgs& a, u64 key) {
     return (c >= 0 && c < a.V) ? (int)column_token(a.d2t, c) : c;
 }
 
-// Candidates of slot j of block b from the per-workgroup partial lists, then
-// the confidence of that slot; lengths[b] (preset to n_pred) is lowered to j
-// when conf < p_min, so it ends at the first such slot (llama.cpp commit
-// 6fed9f6, "spec: add confidence-based draft pruning for DSpark" and
-// "dspark: fold conf_min into p_min").
+// Final step of a proposal, for every block b and slot j: the slot's
+// confidence, with lengths[b] (preset to n_pred) lowered to j when conf <
+// p_min so that it ends at the first such slot (llama.cpp commit 6fed9f6,
+// "spec: add confidence-based draft pruning for DSpark" and "dspark: fold
+// conf_min into p_min"); the token from the running argmax; and the
+// candidates, merged from the per-workgroup partial lists. Two shapes, the
+// same results:
+//  * finalize_group: one workgroup per (slot, block), eight keys per thread
+//    in flight, then a wave merge and an LDS merge;
+//  * finalize_wave: one wave per (block, slot), four per workgroup, 16 keys
+//    per lane in flight. With many pairs a workgroup per pair costs more in
+//    launch and dispatch than in merging (at B = 64, 1024 pairs: 31 -> 22 us);
+//    with few (B = 8: 128 pairs) it spreads the merge over more CUs (12
+//    against 14.5 us).
+
 template <int KL>
-__global__ __launch_bounds__(256) void finalize(FinalArgs a) {
+__global__ __launch_bounds__(256) void finalize_group(FinalArgs a) {
     const int j = blockIdx.x, b = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int B = a.B, n = a.n_pred, k = a.top_k;
@@ -1560,6 +1573,88 @@ __global__ __launch_bounds__(256) void finalize(FinalArgs a) {
             if (lane == 0 && c < a.p_min) atomicMin(a.lengths + b, j);
         }
         if (lane == 0 && a.conf) a.conf[o] = c;
+    }
+}
+
+template <int KL>
+__global__ __launch_bounds__(256) void finalize_wave(FinalArgs a) {
+    // one wave per (block, slot); pair = b * n_pred + j is the output row
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int B = a.B, n = a.n_pred, k = a.top_k;
+    const long o = (long)blockIdx.x * kWaves + wave;
+    if (o >= (long)B * n) return;
+    const int b = (int)(o / n), j = (int)(o - (long)b * n);
+
+    // Adaptive gate: a slot past its block's cut was not drafted, and a block
+    // keeps only its own number of candidates.
+    const int kb = a.top_k_b ? min(max(a.top_k_b[b], 1), k) : k;
+    if (a.gated && j >= a.lengths[b]) {
+        for (int i = lane; i < k; i += kWave) {
+            a.candidates[o * k + i] = -1;
+            if (a.cand_logits) a.cand_logits[o * k + i] = -INFINITY;
+        }
+        if (lane == 0) a.tokens[o] = -1;
+        return;
+    }
+    const u64 win = winner_key(a.winners, a.wstride, j, b);
+
+    // The first keys of the partial lists are loaded before the confidence,
+    // so that both sets of loads are in flight together.
+    constexpr int U = 16;
+    const u64* p = a.partials + ((long)j * B + b) * a.nwg * k;
+    const int cnt = k > 1 ? a.nwg * k : 0;
+    u64 kk[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) kk[u] = lane + u * kWave < cnt ? p[lane + u * kWave] : 0ull;
+
+    // Confidence head (with the adaptive gate it was computed before the chain).
+    if (!a.gated) {
+        float c = 1.0f;
+        if (a.conf_w) {
+            c = slot_conf(a.hidden, a.hidden_f32, a.conf_w, (long)b * a.L + a.i_first + j, a.H, lane);
+            if (lane == 0 && c < a.p_min) atomicMin(a.lengths + b, j);
+        }
+        if (lane == 0 && a.conf) a.conf[o] = c;
+    }
+
+    if (k == 1) {
+        if (lane == 0) {
+            const int t = final_token(a, win);
+            a.tokens[o] = t;
+            a.candidates[o] = t;
+            if (a.cand_logits) a.cand_logits[o] = key_score(win);
+        }
+        return;
+    }
+    u64 list[KL];
+#pragma unroll
+    for (int i = 0; i < KL; ++i) list[i] = 0ull;
+#pragma unroll
+    for (int u = 0; u < U; ++u) topk_insert<KL>(list, kk[u]);
+    for (int e0 = lane + U * kWave; e0 < cnt; e0 += U * kWave) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) kk[u] = e0 + u * kWave < cnt ? p[e0 + u * kWave] : 0ull;
+#pragma unroll
+        for (int u = 0; u < U; ++u) topk_insert<KL>(list, kk[u]);
+    }
+#pragma unroll
+    for (int mask = 32; mask >= 1; mask >>= 1) {
+        u64 other[KL];
+#pragma unroll
+        for (int i = 0; i < KL; ++i) other[i] = shfl_xor_u64(list[i], mask);
+#pragma unroll
+        for (int i = 0; i < KL; ++i) topk_insert<KL>(list, other[i]);
+    }
+    if (lane == 0) {
+        a.tokens[o] = final_token(a, win);
+        if (list[0] != win) atomicOr(a.flags, kFlagInternal);  // internal consistency check
+#pragma unroll
+        for (int i = 0; i < KL; ++i) {
+            if (i < k) {
+                a.candidates[o * k + i] = i < kb ? final_token(a, list[i]) : -1;
+                if (a.cand_logits) a.cand_logits[o * k + i] = i < kb ? key_score(list[i]) : -INFINITY;
+            }
+        }
     }
 }
 
@@ -1790,11 +1885,19 @@ hipError_t launch_gate(const GateArgs& g, hipStream_t stream) {
 }
 
 hipError_t launch_finalize(const FinalArgs& a, hipStream_t stream) {
-    dim3 grid(a.n_pred, a.B), block(256);
-    if (a.top_k <= 1) hipLaunchKernelGGL(finalize<1>, grid, block, 0, stream, a);
-    else if (a.top_k <= 4) hipLaunchKernelGGL(finalize<4>, grid, block, 0, stream, a);
-    else if (a.top_k <= 8) hipLaunchKernelGGL(finalize<8>, grid, block, 0, stream, a);
-    else hipLaunchKernelGGL(finalize<16>, grid, block, 0, stream, a);
+    const long pairs = (long)a.B * a.n_pred;
+    const dim3 block(256);
+#define DSPARK_FINAL(KERNEL, GRID)                                                           \
+    if (a.top_k <= 1) hipLaunchKernelGGL(KERNEL<1>, GRID, block, 0, stream, a);              \
+    else if (a.top_k <= 4) hipLaunchKernelGGL(KERNEL<4>, GRID, block, 0, stream, a);         \
+    else if (a.top_k <= 8) hipLaunchKernelGGL(KERNEL<8>, GRID, block, 0, stream, a);         \
+    else hipLaunchKernelGGL(KERNEL<16>, GRID, block, 0, stream, a);
+    if (pairs >= kFinalWavePairs) {
+        DSPARK_FINAL(finalize_wave, dim3((unsigned)((pairs + kWaves - 1) / kWaves)))
+    } else {
+        DSPARK_FINAL(finalize_group, dim3(a.n_pred, a.B))
+    }
+#undef DSPARK_FINAL
     return hipGetLastError();
 }
 

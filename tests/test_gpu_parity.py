@@ -111,6 +111,12 @@ SMALL = {
     "reduced_vocab": lambda: make_small(4, 7, 176, 4096, 64, top_k=4, layout=BONUS_ANCHOR,
                                         reachable=300, conf=True, p_min=0.5, conf_trend=True,
                                         seed=10),
+    # 512 (block, slot) pairs or more: the one-wave-per-pair finalize
+    "final_wave_k4_conf": lambda: make_small(64, 9, 64, 3000, 16, top_k=4, conf=True, p_min=0.4,
+                                             seed=48),
+    "final_wave_k1": lambda: make_small(130, 4, 64, 2000, 8, top_k=1, conf=True, p_min=0.3, seed=49),
+    "final_wave_k16_bonus": lambda: make_small(70, 9, 64, 1500, 8, top_k=16, layout=BONUS_ANCHOR,
+                                               seed=50),
 }
 
 
@@ -347,6 +353,8 @@ ADAPTIVE = {
                                                 conf_trend=True, layout=BONUS_ANCHOR, seed=62),
     "adaptive_B70": lambda: make_small(70, 5, 64, 2048, 16, top_k=2, conf=True, conf_trend=True,
                                        seed=63),
+    "adaptive_B72_final_wave": lambda: make_small(72, 8, 64, 2048, 16, top_k=4, conf=True,
+                                                  conf_trend=True, seed=64),
 }
 
 
