@@ -332,10 +332,17 @@ def main() -> int:
         gemm_gbs = gemm_bytes / (gemm_ms * 1e-3) / 1e9
         gemm_roof = {"bound": "hbm", "achieved": gemm_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gemm_gbs / PEAK_HBM_GBS}
-    # chain: per slot the B logits rows and markov_w2 are streamed, plus B rank-r gathers
-    # (the adaptive gate runs the chain only up to the longest surviving block)
-    slots_run = int(out.lengths.max().item()) if args.adaptive else n
-    chain_bytes = slots_run * (B * V * 4 + V * r * 2 + B * r * 2)
+    # chain: per slot the B logits rows and markov_w2 are streamed, plus B rank-r gathers;
+    # the adaptive gate runs the chain only up to the longest surviving block, and a
+    # slot streams the logits rows (and gathers) of the blocks still drafting there
+    if args.adaptive:
+        lens = out.lengths.cpu().tolist()
+        slots_run = max(lens)
+        live = [sum(1 for x in lens if x > jj) for jj in range(slots_run)]
+        chain_bytes = sum(lv * V * 4 + V * r * 2 + lv * r * 2 for lv in live)
+    else:
+        slots_run = n
+        chain_bytes = slots_run * (B * V * 4 + V * r * 2 + B * r * 2)
     chain_gbs = chain_bytes / (chain_ms * 1e-3) / 1e9
 
     res = {

@@ -94,6 +94,14 @@ __device__ __forceinline__ int prev_token(const ChainArgs& a, int j, int b, bool
     return 0;
 }
 
+// Adaptive gate: block b was cut before slot j (its confidence fell below its
+// threshold at a slot < j + 1), so slot j is not drafted for it. The chain
+// then streams no logits row for it, inserts and publishes nothing for it,
+// and reads no previous token for it (it published none).
+__device__ __forceinline__ bool block_cut(const ChainArgs& a, int b, int j) {
+    return a.stop != nullptr && a.lengths[b] <= j;
+}
+
 // prev_b for slot j (anchor, or the previous slot's argmax) and the lane's
 // share of markov_w1[prev_b] as MFMA B operand: u[nb][s] holds
 // W1[prev][16 s + 8 (lane / 32) .. + 8] for block bbase + 32 nb + lane % 32.
@@ -344,7 +352,8 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
         } else {
             const int slot = (inst - W_INST) * 64 + lane, row = slot / LR;
             const int c = (slot % LR) ^ swz_rows<LR>(row);
-            const int b = min(bbase + row, B - 1);
+            int b = min(bbase + row, B - 1);
+            if (block_cut(a, b, j)) b = bbase;   // one shared row for every cut block
             src[i] = reinterpret_cast<const char*>(a.logits + ((long)b * a.n_pred + j) * V + 4 * c);
             step[i] = (long)TS * 4;
             dst[i] = W_SLOTS + (inst - W_INST) * 64;
@@ -393,7 +402,8 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
 
     // Previous token of this lane's block (anchor, or the last slot's argmax).
     const int bme = bbase + nbw * 32 + lrow;
-    const int prev = (bme < B && nbw < NB) ? prev_token(a, j, bme, vb == 0) : 0;
+    const bool live = bme < B && !block_cut(a, bme, j);
+    const int prev = (live && nbw < NB) ? prev_token(a, j, bme, vb == 0) : 0;
     // Tile 0, then the markov_w1 rows of prev (MFMA B operand; their address
     // needs prev), then tiles 1 .. NS-2. The loop starts once tile 0 and the
     // W1 rows have landed, with the later tiles still in flight. The W1 rows
@@ -425,7 +435,7 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
     // MFMA runs on whole waves: only the wave-uniform part of the condition may
     // guard it; blocks past B are masked at the inserts.
     const bool wave_on = nbw < NB;
-    const bool active = wave_on && bme < B;
+    const bool active = wave_on && live;
 
     u64 list[KL];
 #pragma unroll
@@ -724,7 +734,8 @@ __global__ __launch_bounds__(256) void chain_step_wave(ChainArgs a, int j) {
         } else {
             const int slot = (i - W_INST) * 64 + lane, row = slot / LR;
             const int c = (slot % LR) ^ swz_rows<LR>(row);
-            const int b = min(bbase + nbw * 32 + row, B - 1);
+            int b = min(bbase + nbw * 32 + row, B - 1);
+            if (block_cut(a, b, j)) b = bbase + nbw * 32;   // one shared row for every cut block
             src[i] = reinterpret_cast<const char*>(a.logits + ((long)b * a.n_pred + j) * V + cbase + 4 * c);
         }
         dst[i] = i * 64;
@@ -763,7 +774,7 @@ __global__ __launch_bounds__(256) void chain_step_wave(ChainArgs a, int j) {
     };
 
     const int bme = bbase + nbw * 32 + lrow;
-    const bool active = bme < B;
+    const bool active = bme < B && !block_cut(a, bme, j);
     const int prev = active ? prev_token(a, j, bme, vb == 0) : 0;
     if (lhalf == 0) s_thr[wave][lrow] = -INFINITY;
     wait_lds_reads();
@@ -1049,9 +1060,10 @@ __global__ __launch_bounds__(256) void chain_step_sparse(ChainArgs a, int j) {
     // the wave's slabs (none for a group past the last block)
     const int sb0 = (int)(nS * wg / GW), sb1 = gbase < B ? (int)(nS * (wg + 1) / GW) : sb0;
     const int bme = gbase + lrow;
-    const bool active = bme < B;
-    // blocks of the group that exist, as a mask over the group's 32 blocks
-    const uint32_t exist = B - gbase >= 32 ? 0xFFFFFFFFu : (B > gbase ? (1u << (B - gbase)) - 1u : 0u);
+    const bool active = bme < B && !block_cut(a, bme, j);
+    // blocks of the group that exist and are not cut, as a mask over the
+    // group's 32 blocks (lanes 0-31 hold them)
+    const uint32_t exist = (uint32_t)(__ballot(active) & 0xFFFFFFFFull);
     // slab maxima of the first pass (register loads issued before the wait
     // below, so they travel with the previous tokens): lane k reads slab
     // pb + k of each of the group's blocks (rows b * n_pred + j)
@@ -1063,7 +1075,7 @@ __global__ __launch_bounds__(256) void chain_step_sparse(ChainArgs a, int j) {
         for (int k = 0; k < 32; ++k) {
             // rows of blocks past B are not read (their row is clamped, the value dropped)
             const float x = col[(long)min(k, B - 1 - gbase) * a.n_pred * nS];
-            sm[k] = gbase + k < B ? x : -INFINITY;
+            sm[k] = (exist >> k) & 1u ? x : -INFINITY;
         }
     };
     if (sb0 < sb1) load_smax(sb0);
