@@ -39,8 +39,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # reported for any other source or workload.
 GEMM_TRAFFIC = {
     "workload": "qwen38_27b_throughput",
-    "source_sha256": "39ec223a819fd624bfea00c7382fb0bfa346c6b2433795d10aba7eb66bff476f",
-    "bytes": 5689567312,
+    "source_sha256": "05455fb9726e035f9ee42c7b47ccb84805b8fc803f2f01b859d1fef50cdc2185",
+    "bytes": 5736282747,
 }
 
 

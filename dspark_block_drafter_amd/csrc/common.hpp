@@ -152,6 +152,68 @@ __device__ __forceinline__ void block_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Largest squared row norm of a bf16 matrix [rows, r], r a multiple of 8,
+// taken by G workgroups (this is group g): a sum of squares of bf16 values in
+// fp32 (every square is exact), raised into *out as fp32 bits (the bits of
+// non-negative floats order as unsigned integers). When a row is a power of
+// two of 16-byte chunks (r = 8, 16, ..., 256) the wave reads the matrix as
+// consecutive 16-byte chunks, 16 per lane in flight, and sums each row over
+// the aligned group of lanes that hold its chunks; otherwise each thread sums
+// whole rows.
+__device__ __forceinline__ void row_norm_part(const uint16_t* w, long rows, int r, int g, int G,
+                                              uint32_t* out) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int nw = blockDim.x >> 6, wave = tid >> 6;
+    const int cpr = r >> 3;   // 16-byte chunks per row
+    float best = 0.0f;
+    if ((cpr & (cpr - 1)) == 0 && cpr <= 64) {
+        constexpr int U = 16;
+        const long chunks = rows * cpr;
+        const u32x4* p = reinterpret_cast<const u32x4*>(w);
+        // wave-steps of 64 U chunks; wave (g, wave) takes steps g * nw + wave + k * G * nw
+        for (long base = ((long)g * nw + wave) * 64 * U; base < chunks; base += (long)G * nw * 64 * U) {
+            u32x4 x[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const long c = base + u * 64 + lane;
+                x[u] = c < chunks ? p[c] : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float s = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float lo = bf16_lo(x[u][q]), hi = bf16_hi(x[u][q]);
+                    s += lo * lo;
+                    s += hi * hi;
+                }
+                // the row's sum over its cpr lanes (aligned groups of the 64)
+                for (int m = 1; m < cpr; m <<= 1) s += __shfl_xor(s, m, kWave);
+                best = fmaxf(best, s);
+            }
+        }
+    } else {
+        const int nt = blockDim.x;
+        for (long row = (long)g * nt + tid; row < rows; row += (long)G * nt) {
+            const uint16_t* q0 = w + row * r;
+            float s = 0.0f;
+            for (int k = 0; k < r; k += 8) {
+                const u32x4 x = *reinterpret_cast<const u32x4*>(q0 + k);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float lo = bf16_lo(x[q]), hi = bf16_hi(x[q]);
+                    s += lo * lo;
+                    s += hi * hi;
+                }
+            }
+            best = fmaxf(best, s);
+        }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) best = fmaxf(best, __shfl_xor(best, m, kWave));
+    if (lane == 0) atomicMax(out, __float_as_uint(best));
+}
+
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef __attribute__((address_space(3))) char lds_char;
 // Cache policy of a load that is read once (non-temporal: gfx950 "nt").

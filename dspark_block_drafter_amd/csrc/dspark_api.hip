@@ -100,6 +100,7 @@ struct ChainExtras {
     int vocab = 0;                    // target vocabulary (rows of markov_w1); 0: V
     const float* p_min_b = nullptr;   // adaptive gate: per-block thresholds, conf before the chain
     const int32_t* top_k_b = nullptr; // adaptive: candidates kept per block
+    bool narrow_slabs = false;        // the projection writes kSlabCols-column slab maxima (4-bit head)
 };
 
 // Arguments of the chain kernels over V columns. With `bounded` the chain
@@ -144,7 +145,9 @@ ChainArgs chain_args(const float* logits, const uint16_t* w1, const uint16_t* w2
     c.sparse = sparse ? 1 : 0;
     // the pruned form reads slabs of kSlabCols; otherwise the four-wave
     // projection takes one wave's columns per slab
-    c.slab_cols = !sparse && gemm_four_wave(B * n_pred, H, L, n_pred, hidden_f32) ? kSlabColsWide : kSlabCols;
+    c.slab_cols = !sparse && !x.narrow_slabs && gemm_four_wave(B * n_pred, H, L, n_pred, hidden_f32)
+                      ? kSlabColsWide
+                      : kSlabCols;
     return c;
 }
 
@@ -307,7 +310,7 @@ int check_q4(int B, int L, int H, int V, int layout, const void* lm_head_q4) {
 
 int project_q4(const void* hidden, int hidden_dtype, const void* lm_head_q4, const float* bias,
                int B, int L, int H, int V, int layout, float* logits, void* prep,
-               hipStream_t stream) {
+               hipStream_t stream, const ChainArgs* c = nullptr) {
     Q4Args q{};
     q.i_first = first_pred(layout);
     q.n_pred = L - q.i_first;
@@ -324,7 +327,19 @@ int project_q4(const void* hidden, int hidden_dtype, const void* lm_head_q4, con
     q.packed = static_cast<const uint8_t*>(lm_head_q4);
     q.bias = bias;
     q.out = logits;
-    clear_pending_error();
+    if (c != nullptr && c->smax != nullptr) {
+        // the top-k bound: slab maxima, and the norm workgroups when there is a Markov term
+        q.smax = const_cast<float*>(c->smax);
+        if (c->r > 0) {
+            q.w2 = c->w2;
+            q.w1 = c->w1;
+            q.w_rows = V;
+            q.w_rank = c->r;
+            q.norm_groups = kW2NormGroups;
+            q.w2n2 = c->w2n2;
+            q.w1n2 = c->w1n2;   // (nullptr: markov_w2 only)
+        }
+    }
     return hip_status(launch_lmhead_q4(q, stream));
 }
 
@@ -573,6 +588,7 @@ int dspark_logits_q4(const void* hidden, int hidden_dtype, const void* lm_head_q
     if (!workspace || reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
         return DSPARK_ERR_WORKSPACE;
     if (workspace_bytes < q4_prep_bytes(B * (L - first_pred(layout)), H)) return DSPARK_ERR_WORKSPACE;
+    clear_pending_error();
     return project_q4(hidden, hidden_dtype, lm_head_q4, lm_head_bias, B, L, H, V, layout, logits,
                       workspace, static_cast<hipStream_t>(stream));
 }
@@ -602,14 +618,24 @@ int dspark_propose_q4(const void* hidden, int hidden_dtype, const void* lm_head_
     hipStream_t s = static_cast<hipStream_t>(stream);
     // [chain workspace][preparation]: the flags word stays at offset 0
     void* prep = static_cast<char*>(workspace) + dspark_workspace_bytes(B, L, V, top_k, layout);
-    // the 4-bit projection leaves no slab maxima: the chain runs unbounded
-    const ChainArgs c = chain_args(logits, markov_w1, markov_w2, ChainExtras(), anchors, B, L, H, V, r,
-                                   layout, top_k, hidden_dtype == DSPARK_HIDDEN_F32, workspace, lengths,
-                                   false);
-    st = project_q4(hidden, hidden_dtype, lm_head_q4, lm_head_bias, B, L, H, V, layout, logits, prep, s);
+    // With the bound, the 4-bit projection writes 64-column slab maxima and
+    // carries the norm workgroups, as the bf16 one does; chain_init (which
+    // zeroes the norm words) goes first. Its epilogue pays only where the chain
+    // prunes slabs with it (Qwen3.6-27B shape, 64 blocks of 16: 4.52 ms per
+    // step unbounded, 4.64 ms with the bound filtering top-k inserts; 16
+    // blocks, pruned: 0.889 -> 0.849 ms), so other shapes run unbounded.
+    ChainExtras x;
+    x.narrow_slabs = true;
+    const bool prune = B <= 32 && chain_sparse(V, r);
+    const ChainArgs c = chain_args(logits, markov_w1, markov_w2, x, anchors, B, L, H, V, r, layout,
+                                   top_k, hidden_dtype == DSPARK_HIDDEN_F32, workspace, lengths, prune);
+    clear_pending_error();
+    if (launch_chain_init(c, s) != hipSuccess) return DSPARK_ERR_HIP;
+    st = project_q4(hidden, hidden_dtype, lm_head_q4, lm_head_bias, B, L, H, V, layout, logits, prep, s,
+                    &c);
     if (st != DSPARK_OK) return st;
-    return run_chain(c, false, hidden, hidden_dtype, ChainExtras(), conf_w, B, L, H, V, layout, top_k,
-                     p_min, workspace, tokens, candidates, cand_logits, conf, lengths, s);
+    return run_chain(c, true, hidden, hidden_dtype, x, conf_w, B, L, H, V, layout, top_k, p_min,
+                     workspace, tokens, candidates, cand_logits, conf, lengths, s);
 }
 
 int dspark_verify(const int32_t* candidates, const int32_t* lengths, const int32_t* target, int B,

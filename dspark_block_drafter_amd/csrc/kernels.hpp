@@ -73,6 +73,15 @@ struct Q4Args {
     const uint8_t* packed;   // the packed head
     const float* bias;       // [V] or nullptr
     float* out;              // [M, V]
+    float* smax;             // slab maxima [M][ceil(V / kSlabCols)] (the top-k bound), or nullptr
+    // With w2n2: norm_groups extra workgroups after the projection's raise the
+    // largest squared row norms of markov_w2 [w_rows, w_rank] (and, with w1n2,
+    // of markov_w1) into the two words, zeroed before (as GemmArgs).
+    const uint16_t* w2;
+    const uint16_t* w1;
+    int w_rows, w_rank, norm_groups;
+    uint32_t* w2n2;
+    uint32_t* w1n2;
     int M, V, H, G, GQ, T16;
     int L, n_pred, i_first;  // row m reads hidden row (m / n_pred) * L + i_first + m % n_pred
 };

@@ -167,7 +167,7 @@ __global__ __launch_bounds__(256) void q4_prep(Q4Args a) {
 // The 136 sum_e x_me of a block is produced by one more MFMA per row tile
 // and block, with B = -136 in every slot (exact in bf16), and enters the
 // code MFMAs as their C input: they return sum_e x_me (q - 8) directly.
-template <int FM, int CTW, int NS>
+template <int FM, int CTW, int NS, bool SMAX>
 __global__ __launch_bounds__(256) void lmhead_q4(Q4Args a) {
     constexpr int BM = 16 * FM;
     constexpr int AB = BM * 256;                   // A tile bytes per stage
@@ -183,13 +183,19 @@ __global__ __launch_bounds__(256) void lmhead_q4(Q4Args a) {
     const int M = a.M, V = a.V, GQ = a.GQ;
     const int nrb = (M + BM - 1) / BM;
     const int ncu = (a.T16 + 4 * CTW - 1) / (4 * CTW);
+    const int nunits = nrb * ncu;
+    if ((int)blockIdx.x >= nunits) {
+        // a norm workgroup, in the launch's last, partly filled round
+        const int g = blockIdx.x - nunits;
+        row_norm_part(a.w2, a.w_rows, a.w_rank, g, a.norm_groups, a.w2n2);
+        if (a.w1n2 != nullptr) row_norm_part(a.w1, a.w_rows, a.w_rank, g, a.norm_groups, a.w1n2);
+        return;
+    }
     // the row blocks of one column unit are consecutive; consecutive
     // workgroups of one XCD (blockIdx % 8) get consecutive units, so a unit's
     // codes come into one L2
-    const int nwg = gridDim.x;
-    const int bid = (nwg & 7) == 0 ? (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+    const int bid = (nunits & 7) == 0 ? (blockIdx.x & 7) * (nunits >> 3) + (blockIdx.x >> 3) : blockIdx.x;
     const int cu = bid / nrb, rb = bid - cu * nrb;
-    if (cu >= ncu) return;   // the whole workgroup
     const int m0 = rb * BM, t0 = cu * 4 * CTW + wave * CTW;
 
     // per-lane sources at quad 0 and the LDS offsets (in a stage) of this wave's loads
@@ -318,6 +324,69 @@ __global__ __launch_bounds__(256) void lmhead_q4(Q4Args a) {
         stage = stage + 1 == NS ? 0 : stage + 1;
     }
 
+    // Slab maxima (the chain's top-k bound): per row, the largest logit (bias
+    // included) over each slab of kSlabCols = 64 columns. A wave's columns
+    // are a whole slab (CTW = 4) or half of one (CTW = 2: waves w and w ^ 1
+    // share it). Lane (c, kq) takes the maximum over its CTW columns, then
+    // over the 16 lanes of its kq (lane bits 0-3).
+    if constexpr (SMAX) {
+        static_assert(CTW == 2 || CTW == 4, "a wave holds half a slab or a whole one");
+        const int nslab = (V + kSlabCols - 1) / kSlabCols;
+        float mx[FM][4];
+#pragma unroll
+        for (int f = 0; f < FM; ++f)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx[f][i] = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < CTW; ++j) {
+            const int v = 16 * (t0 + j) + c;
+            if (v >= V) continue;
+            const float b = a.bias ? a.bias[v] : 0.0f;
+#pragma unroll
+            for (int f = 0; f < FM; ++f)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mx[f][i] = fmaxf(mx[f][i], acc[f][j][i] + b);
+        }
+#pragma unroll
+        for (int f = 0; f < FM; ++f)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int x = 1; x < 16; x <<= 1) mx[f][i] = fmaxf(mx[f][i], __shfl_xor(mx[f][i], x, kWave));
+        bool writer = c == 0;
+        if constexpr (CTW == 2) {
+            // The pair exchanges its halves through the ring's first bytes,
+            // once every wave is past its last read of the ring. (A second
+            // LDS array would make the compiler order every ring read after
+            // all copies in flight: a vmcnt(0) in the main loop, 20% slower.)
+            float* s_half = reinterpret_cast<float*>(smem);
+            __syncthreads();
+            if (c == 0) {
+#pragma unroll
+                for (int f = 0; f < FM; ++f)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) s_half[wave * 16 * FM + 16 * f + 4 * kq + i] = mx[f][i];
+            }
+            __syncthreads();
+#pragma unroll
+            for (int f = 0; f < FM; ++f)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    mx[f][i] = fmaxf(mx[f][i], s_half[(wave ^ 1) * 16 * FM + 16 * f + 4 * kq + i]);
+            writer = writer && (wave & 1) == 0;   // the even wave of the pair writes the slab
+        }
+        const int slab = 16 * t0 / kSlabCols;
+        if (writer && slab < nslab) {
+#pragma unroll
+            for (int f = 0; f < FM; ++f)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int m = m0 + 16 * f + 4 * kq + i;
+                    if (m < M) a.smax[(size_t)m * nslab + slab] = mx[f][i];
+                }
+        }
+    }
+
     // + bias, fp32 store (lane (c, kq) holds rows 4 kq + i of column c)
 #pragma unroll
     for (int j = 0; j < CTW; ++j) {
@@ -338,7 +407,9 @@ template <int FM, int CTW, int NS>
 hipError_t run_q4(const Q4Args& a, hipStream_t stream) {
     const long nrb = (a.M + 16 * FM - 1) / (16 * FM);
     const long ncu = (a.T16 + 4 * CTW - 1) / (4 * CTW);
-    hipLaunchKernelGGL((lmhead_q4<FM, CTW, NS>), dim3((unsigned)(nrb * ncu)), dim3(256), 0, stream, a);
+    const dim3 grid((unsigned)(nrb * ncu + (a.w2n2 ? a.norm_groups : 0)));
+    if (a.smax) hipLaunchKernelGGL((lmhead_q4<FM, CTW, NS, true>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((lmhead_q4<FM, CTW, NS, false>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

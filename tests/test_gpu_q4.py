@@ -136,12 +136,30 @@ def test_propose_q4(dev, orc, name):
          f"near ties {sum(r['near_tie'] for r in reps)}")
 
 
-def test_propose_q4_equals_chain_on_q4_logits(dev, orc):
-    """The proposal is the chain of the library run on the q4 projections."""
+BOUNDED = {
+    # The 4-bit call takes the bound where the chain prunes slabs with it (one
+    # block group, V % 4 == 0, rank up to 128): pruned_*, lists16_*. Elsewhere
+    # it runs unbounded: direct (V % 4 != 0) and the two-per-CU ring (two
+    # groups). Every case must equal the unbounded chain bit for bit.
+    "direct_V2222": lambda: make_small(6, 9, 320, 2222, 16, top_k=4, conf=True, p_min=0.4, seed=83),
+    "pruned_B8": lambda: make_small(8, 6, 256, 40000, 64, top_k=4, seed=85),
+    "pruned_conf_B16": lambda: make_small(16, 5, 160, 24000, 48, top_k=8, conf=True, p_min=0.35,
+                                          seed=88),
+    "two_groups_B40": lambda: make_small(40, 4, 128, 30000, 128, top_k=4, conf=True, p_min=0.3,
+                                         seed=86),
+    "lists16_B12": lambda: make_small(12, 5, 96, 20000, 32, top_k=16, seed=87),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BOUNDED))
+def test_propose_q4_equals_chain_on_q4_logits(dev, orc, name):
+    """The proposal (with the top-k bound from the 4-bit projection's slab
+    maxima where the chain prunes) is the unbounded chain of the library run
+    on the q4 projections, bit for bit; and it passes the oracle's checker."""
     import torch
     import dspark_block_drafter_amd as dsp
     from devutil import run_propose_q4, to_device_q4, to_host
-    q = quantize_q4(make_small(6, 9, 320, 2222, 16, top_k=4, conf=True, p_min=0.4, seed=83), "round")
+    q = quantize_q4(BOUNDED[name](), "round")
     c = q.cfg
     d = to_device_q4(q)
     a = to_host(run_propose_q4(q, dev=d))
@@ -153,6 +171,7 @@ def test_propose_q4_equals_chain_on_q4_logits(dev, orc):
     assert np.array_equal(a["logits"], z.cpu().numpy())
     for k in ("tokens", "candidates", "cand_logits", "conf", "lengths"):
         assert np.array_equal(a[k], b[k]), k
+    _check_q4(orc, q, a)
 
 
 FULL = ["qwen3_8b", "gemma4_26b_a4b", "qwen38_27b_tree", "qwen38_27b_throughput"]
