@@ -51,6 +51,73 @@ __device__ __forceinline__ int prev_token(const ChainArgs& a, int j, int b, bool
     return 0;
 }
 
+// The previous tokens of a group of 32 blocks through LDS. A step kernel
+// copies the words they come from (slot j > 0: the previous slot's
+// kWinnerWays running-argmax words of blocks gbase .. gbase + 31, 2 KB;
+// slot 0: the anchors) direct to LDS ahead of the tile copies, which do not
+// depend on them; waits for them with an explicit count (loads complete in
+// issue order, so the tiles stay in flight); and reads them back. A register
+// load among the copies would instead be waited for with every copy in
+// flight. kPrevChunks 16-byte chunks hold one group's copy. The caller
+// copies only for a group that holds a block (gbase < B): its 32 words of a
+// way then lie inside the way's row (winners_stride rounds B up to 32).
+constexpr int kPrevChunks = 128;
+
+__device__ __forceinline__ void copy_prev(const ChainArgs& a, int j, int gbase, lds_char* dst) {
+    const int lane = threadIdx.x & 63;
+    if (j == 0) {
+        // lane l's anchor to byte 4 l: lanes 0-31 hold blocks gbase + l
+        const int b = min(gbase + (lane & 31), a.B - 1);
+        __builtin_amdgcn_global_load_lds((const void*)(a.anchors + b), (lds_ptr)dst, 4, 0, 0);
+    } else {
+        // chunk 64 i + l: way 4 i + l / 16, blocks gbase + 2 (l % 16) and the next
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int way = 4 * i + (lane >> 4);
+            const unsigned long long* w =
+                a.winners + ((long)(j - 1) * kWinnerWays + way) * a.wstride + gbase + 2 * (lane & 15);
+            __builtin_amdgcn_global_load_lds((const void*)w, (lds_ptr)(dst + i * 64 * 16), 16, 0, 0);
+        }
+    }
+}
+
+// The previous token of block gbase + k from copy_prev's copy at src (after
+// the wait for it), as prev_token gives it.
+__device__ __forceinline__ int prev_from_copy(const ChainArgs& a, int j, const void* src, int k, bool report) {
+    typedef const __attribute__((address_space(3))) int32_t lds_i32;
+    typedef const __attribute__((address_space(3))) unsigned long long lds_u64;
+    long t;
+    uint32_t bad;
+    if (j == 0) {
+        t = ((lds_i32*)src)[k];
+        bad = kFlagBadAnchor;
+    } else {
+        lds_u64* w = (lds_u64*)src;
+        unsigned long long m = w[k];
+#pragma unroll
+        for (int i = 1; i < kWinnerWays; ++i) {
+            const unsigned long long x = w[i * 32 + k];
+            m = x > m ? x : m;
+        }
+        const int c = key_id(m);
+        if (c < 0 || c >= a.V) {
+            t = -1;
+        } else if (a.d2t == nullptr) {
+            t = c;
+        } else {
+            // A register load among the copies: this path waits for every
+            // load in flight here, so that the paths without one do not
+            // inherit the wait where they join.
+            t = a.d2t[c];
+            wait_vmcnt<0>();
+        }
+        bad = kFlagBadD2t;
+    }
+    if (t >= 0 && t < a.vocab) return (int)t;
+    if (report) atomicOr(a.flags, bad);
+    return 0;
+}
+
 // Adaptive gate: block b was cut before slot j (its confidence fell below its
 // threshold at a slot < j + 1), so slot j is not drafted for it. The chain
 // then streams no logits row for it, inserts and publishes nothing for it,

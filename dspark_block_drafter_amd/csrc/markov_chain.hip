@@ -182,15 +182,27 @@ __global__ __launch_bounds__(256) void row_kth(const float* smax, int nslab, flo
 // bbase + lane into s_kth[64] (blocks past B repeat block B - 1), and, by the
 // last wave, of the markov_w2 (and, with s_w1n2, markov_w1) norm word into
 // all 64 words of s_w2n2 (s_w1n2).
+// The destinations are addressed through bases the compiler cannot trace to
+// the arrays (the readers wait explicitly): a copy it can attribute to an
+// array makes it wait for every copy in flight before any later LDS read it
+// cannot tell apart from that array.
 __device__ __forceinline__ void load_bound(const ChainArgs& a, int j, int bbase, float* s_kth,
                                            uint32_t* s_w2n2, int wave, int lane, uint32_t* s_w1n2 = nullptr) {
     if (wave == 0) {
         const int b = min(bbase + lane, a.B - 1);
-        __builtin_amdgcn_global_load_lds((const void*)(a.kth + (long)b * a.n_pred + j), (lds_ptr)s_kth, 4, 0, 0);
+        lds_char* d = (lds_char*)(lds_ptr)s_kth;
+        asm volatile("" : "+s"(d));
+        __builtin_amdgcn_global_load_lds((const void*)(a.kth + (long)b * a.n_pred + j), (lds_ptr)d, 4, 0, 0);
     }
     if (wave == kWaves - 1) {
-        __builtin_amdgcn_global_load_lds((const void*)a.w2n2, (lds_ptr)s_w2n2, 4, 0, 0);
-        if (s_w1n2 && a.w1n2) __builtin_amdgcn_global_load_lds((const void*)a.w1n2, (lds_ptr)s_w1n2, 4, 0, 0);
+        lds_char* d = (lds_char*)(lds_ptr)s_w2n2;
+        asm volatile("" : "+s"(d));
+        __builtin_amdgcn_global_load_lds((const void*)a.w2n2, (lds_ptr)d, 4, 0, 0);
+        if (s_w1n2 && a.w1n2) {
+            lds_char* d1 = (lds_char*)(lds_ptr)s_w1n2;
+            asm volatile("" : "+s"(d1));
+            __builtin_amdgcn_global_load_lds((const void*)a.w1n2, (lds_ptr)d1, 4, 0, 0);
+        }
     }
 }
 
@@ -311,33 +323,52 @@ __global__ __launch_bounds__(256) void chain_step_pipe(ChainArgs a, int j) {
     // Previous token of this lane's block (anchor, or the last slot's argmax).
     const int bme = bbase + nbw * 32 + lrow;
     const bool live = bme < B && !block_cut(a, bme, j);
-    const int prev = (live && nbw < NB) ? prev_token(a, j, bme, vb == 0) : 0;
-    // Tile 0, then the markov_w1 rows of prev (MFMA B operand; their address
-    // needs prev), then tiles 1 .. NS-2. The loop starts once tile 0 and the
-    // W1 rows have landed, with the later tiles still in flight. The W1 rows
+    // The copy of the previous tokens' words (each wave its own, after the
+    // W1 rows in stage NS-1), tiles 0 .. NS-2, then the tokens and the
+    // markov_w1 rows of prev (MFMA B operand; their address needs prev). The
+    // words land first, so the tiles stream during the tokens' two round
+    // trips. The loop starts once all of these have landed. The W1 rows
     // travel direct to LDS like the tiles (a register load would need a wait
     // for every older load, the whole ring), into stage NS-1, which the first
     // step refills only after the barrier that follows their reads: one copy
-    // per block group, loaded by its first wave. The number of loads issued
-    // after the W1 rows is fixed: a workgroup owns n >= 1 tiles (there are at
-    // most as many workgroups as tiles), and a stage past n - 1 gets a second
-    // copy of the last tile, which no iteration reads. Lanes of blocks past B
-    // read row 0 (their scores are never inserted); chunks past the rank are
-    // zeroed when read.
+    // per block group, loaded by its first wave. A workgroup owns n >= 1
+    // tiles (there are at most as many workgroups as tiles), and a stage past
+    // n - 1 gets a second copy of the last tile, which no iteration reads, so
+    // the number of loads in flight is fixed. Lanes of blocks past B read row
+    // 0 (their scores are never inserted); chunks past the rank are zeroed
+    // when read. (Without markov_w1 rows, r = 0, the token is read directly.)
     static_assert(NS >= 2, "a stage in use and one in flight at least");
     static_assert(NB * RS * 64 <= STAGE, "W1 rows fit stage NS - 1");
-    issue(0, t0);
-    if (RS > 0 && vb == 0 && nbw < NB) {
-#pragma unroll
-        for (int s = 0; s < RS; ++s) {
-            const int k0 = s * 16 + lhalf * 8;
-            __builtin_amdgcn_global_load_lds((const void*)(a.w1 + (long)prev * r + (k0 < r ? k0 : 0)),
-                                             (lds_ptr)(ring_dma + ((NS - 1) * STAGE + (nbw * RS + s) * 64) * 16), 16, 0, 0);
-        }
+    constexpr int PREV_OFF = NB * RS * 64;   // the waves' copies of the previous tokens' words
+    static_assert(RS == 0 || PREV_OFF + kWaves * kPrevChunks <= STAGE, "previous tokens fit stage NS - 1");
+    int prev = 0;
+    if constexpr (RS > 0) {
+        if (nbw < NB && bbase + nbw * 32 < B)
+            copy_prev(a, j, bbase + nbw * 32, ring_dma + ((NS - 1) * STAGE + PREV_OFF + wave * kPrevChunks) * 16);
+    } else {
+        prev = (live && nbw < NB) ? prev_token(a, j, bme, vb == 0) : 0;
     }
+    issue(0, t0);
 #pragma unroll
     for (int t = 1; t < NS - 1; ++t) issue(t, t0 + min(t, n - 1));
-    wait_vmcnt<(NS - 2) * LW>();
+    if constexpr (RS > 0) {
+        wait_vmcnt<(NS - 1) * LW>();   // the words: older than every tile copy
+        asm volatile("" ::: "memory");
+        // (read through the copies' base: an address the compiler can trace
+        // to the ring would make it wait for every copy in flight first)
+        if (live && nbw < NB)
+            prev = prev_from_copy(a, j, (const void*)(ring_dma + ((NS - 1) * STAGE + PREV_OFF + wave * kPrevChunks) * 16),
+                                  lrow, vb == 0);
+        if (vb == 0 && nbw < NB) {
+#pragma unroll
+            for (int s = 0; s < RS; ++s) {
+                const int k0 = s * 16 + lhalf * 8;
+                __builtin_amdgcn_global_load_lds((const void*)(a.w1 + (long)prev * r + (k0 < r ? k0 : 0)),
+                                                 (lds_ptr)(ring_dma + ((NS - 1) * STAGE + (nbw * RS + s) * 64) * 16), 16, 0, 0);
+            }
+        }
+    }
+    wait_vmcnt<0>();
     u32x4 u[RS > 0 ? RS : 1];   // W1 rows (MFMA B operand), read after the barrier
 
     // MFMA runs on whole waves: only the wave-uniform part of the condition may
@@ -683,20 +714,31 @@ __global__ __launch_bounds__(256) void chain_step_wave(ChainArgs a, int j) {
 
     const int bme = bbase + nbw * 32 + lrow;
     const bool active = bme < B && !block_cut(a, bme, j);
-    const int prev = active ? prev_token(a, j, bme, vb == 0) : 0;
-    if (lhalf == 0) s_thr[wave][lrow] = -INFINITY;
-    wait_lds_reads();
-    if (bounded) wait_vmcnt<0>();   // the bound's copies (and the previous tokens)
-    block_barrier();   // every bound is set before any wave reads it
-
-    // Tile 0, the markov_w1 rows of prev (the MFMA B operand) into stage
-    // NS-1, tiles 1 .. NS-2; then, once tile 0 and the W1 rows have landed and
-    // the rows are in registers, tile NS-1 into stage NS-1. A stage past the
-    // last tile gets a second copy of it (no iteration reads it), so the
-    // number of copies in flight is fixed. Chunks past the rank are zeroed
-    // when read.
-    issue(0, 0);
+    // The copy of the previous tokens' words into stage NS-1, tiles 0 .. NS-2,
+    // then the tokens and the markov_w1 rows of prev (the MFMA B operand)
+    // into stage NS-1 over the read copy. The words land first, so the tiles
+    // stream during the tokens' two round trips. Once all of these (and the
+    // bound's copies) have landed and every wave has set its bounds, the rows
+    // go to registers and tile NS-1 into stage NS-1. A stage past the last
+    // tile gets a second copy of it (no iteration reads it), so the number of
+    // copies in flight is fixed. Chunks past the rank are zeroed when read.
+    // (Without markov_w1 rows, r = 0, the token is read directly.)
+    static_assert(RS == 0 || kPrevChunks <= STAGE, "previous tokens fit a stage");
+    int prev = 0;
     if constexpr (RS > 0) {
+        if (bbase + nbw * 32 < B) copy_prev(a, j, bbase + nbw * 32, ring_dma + (NS - 1) * STAGE * 16);
+    } else {
+        prev = active ? prev_token(a, j, bme, vb == 0) : 0;
+    }
+    issue(0, 0);
+#pragma unroll
+    for (int t = 1; t < NS - 1; ++t) issue(t, min(t, n - 1));
+    if constexpr (RS > 0) {
+        wait_vmcnt<(NS - 1) * LW>();   // the words: older than every tile copy
+        asm volatile("" ::: "memory");
+        if (active) prev = prev_from_copy(a, j, (const void*)(ring_dma + (NS - 1) * STAGE * 16), lrow, vb == 0);
+        wait_lds_reads();   // the copy is read before the W1 rows replace it
+        asm volatile("" ::: "memory");
 #pragma unroll
         for (int s = 0; s < RS; ++s) {
             const int k0 = s * 16 + lhalf * 8;
@@ -704,9 +746,10 @@ __global__ __launch_bounds__(256) void chain_step_wave(ChainArgs a, int j) {
                                              (lds_ptr)(ring_dma + ((NS - 1) * STAGE + s * 64) * 16), 16, 0, 0);
         }
     }
-#pragma unroll
-    for (int t = 1; t < NS - 1; ++t) issue(t, min(t, n - 1));
-    wait_vmcnt<(NS - 2) * LW>();
+    if (lhalf == 0) s_thr[wave][lrow] = -INFINITY;
+    wait_lds_reads();
+    wait_vmcnt<0>();   // tiles 0 .. NS-2, the W1 rows, the bound's copies
+    block_barrier();   // every bound is set before any wave reads it
     asm volatile("" ::: "memory");
     u32x4 u[RS > 0 ? RS : 1];
 #pragma unroll
