@@ -39,8 +39,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # reported for any other source or workload.
 GEMM_TRAFFIC = {
     "workload": "qwen38_27b_throughput",
-    "source_sha256": "05455fb9726e035f9ee42c7b47ccb84805b8fc803f2f01b859d1fef50cdc2185",
-    "bytes": 5736282747,
+    "source_sha256": "6aaf425b8a82f80e734bb6da1d0d745c2844622dc6c9f2588090d0a7e190595b",
+    "bytes": 5594072754,
 }
 
 

@@ -214,6 +214,15 @@ __device__ __forceinline__ void row_norm_part(const uint16_t* w, long rows, int 
     if (lane == 0) atomicMax(out, __float_as_uint(best));
 }
 
+// XCD-aware order of T work units: dispatch sends workgroup i to XCD i % 8,
+// so XCD x receives q + (x < rem) of them (T = 8 q + rem); give it that many
+// consecutive units, in XCD order, so neighbouring units share an L2. (For
+// T % 8 == 0: (i % 8) (T / 8) + i / 8.)
+__device__ __forceinline__ int xcd_unit(int i, int T) {
+    const int x = i & 7, l = i >> 3, q = T >> 3, rem = T & 7;
+    return x * q + (x < rem ? x : rem) + l;
+}
+
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef __attribute__((address_space(3))) char lds_char;
 // Cache policy of a load that is read once (non-temporal: gfx950 "nt").

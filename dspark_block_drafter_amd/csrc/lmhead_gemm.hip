@@ -194,7 +194,7 @@ __global__ __launch_bounds__(64 * WM * WN) void lmhead_gemm(GemmArgs a) {
     }
     // XCD-aware order: dispatch sends block i to XCD i % 8; give each XCD a
     // contiguous run of tiles, M fastest, so the M tiles of an N slab share an L2.
-    const int sid = (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
+    const int sid = xcd_unit(bid, T);
     const int m0 = (sid % nMT) * BM, n0 = (sid / nMT) * BN;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -350,7 +350,7 @@ __global__ __launch_bounds__(64 * WM * WN) void lmhead_gemm_dma(GemmArgs a) {
         w2_norm_part(a, bid - T);
         return;
     }
-    const int sid = (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
+    const int sid = xcd_unit(bid, T);
     const int m0 = (sid % nMT) * BM, n0 = (sid / nMT) * BN;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -474,7 +474,7 @@ __global__ __launch_bounds__(256) void lmhead_gemm_w4(GemmArgs a) {
         w2_norm_part(a, bid - T);
         return;
     }
-    const int sid = (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
+    const int sid = xcd_unit(bid, T);
     const int m0 = (sid % nMT) * BM, n0 = (sid / nMT) * BN;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

@@ -194,7 +194,7 @@ __global__ __launch_bounds__(256) void lmhead_q4(Q4Args a) {
     // the row blocks of one column unit are consecutive; consecutive
     // workgroups of one XCD (blockIdx % 8) get consecutive units, so a unit's
     // codes come into one L2
-    const int bid = (nunits & 7) == 0 ? (blockIdx.x & 7) * (nunits >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+    const int bid = xcd_unit(blockIdx.x, nunits);
     const int cu = bid / nrb, rb = bid - cu * nrb;
     const int m0 = rb * BM, t0 = cu * 4 * CTW + wave * CTW;
 
