@@ -1243,49 +1243,57 @@ __global__ __launch_bounds__(256) void chain_step_direct(ChainArgs a, int j) {
 
 // Confidence of one slot on one wave: float(sigmoid(hidden_row . conf_w)),
 // fp32 hidden rounded to bf16 first.
-__device__ __forceinline__ float slot_conf(const void* hidden, int hidden_f32, const uint16_t* conf_w,
-                                           long row, int H, int lane) {
+template <bool F32>
+__device__ __forceinline__ float slot_conf_dot(const void* hidden, const uint16_t* conf_w, long row, int H,
+                                               int lane) {
     // Lane l sums h = 8l + 512i .. + 8 for i = 0, 1, ... in that order. The
-    // loads of four such chunks go out together (a chunk past H reads the
-    // lane's first chunk again and adds nothing).
-    constexpr int U = 4;
+    // loads of sixteen such chunks (H up to 8192 in one round) go out
+    // together, raw, and are converted after (a chunk past H reads the lane's
+    // first chunk again and adds nothing). The hidden dtype is a template
+    // parameter: a branch on it among the loads would have them waited for
+    // one chunk at a time.
+    constexpr int U = 16;
     float s = 0.0f;
     for (int h0 = lane * 8; h0 < H; h0 += 64 * 8 * U) {
-        u32x4 cw[U];
-        float x[U][8];
+        u32x4 cw[U], hv[U];
+        f32x4 hf[F32 ? U : 1][2];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int h = h0 + u * 64 * 8 < H ? h0 + u * 64 * 8 : lane * 8;
             cw[u] = *reinterpret_cast<const u32x4*>(conf_w + h);
-            if (hidden_f32) {
+            if constexpr (F32) {
                 const f32x4* hp = reinterpret_cast<const f32x4*>(static_cast<const float*>(hidden) + row * H + h);
-                const f32x4 x0 = hp[0], x1 = hp[1];
-                const uint32_t p0 = pack_bf16x2(x0[0], x0[1]), p1 = pack_bf16x2(x0[2], x0[3]);
-                const uint32_t p2 = pack_bf16x2(x1[0], x1[1]), p3 = pack_bf16x2(x1[2], x1[3]);
-                x[u][0] = bf16_lo(p0); x[u][1] = bf16_hi(p0); x[u][2] = bf16_lo(p1); x[u][3] = bf16_hi(p1);
-                x[u][4] = bf16_lo(p2); x[u][5] = bf16_hi(p2); x[u][6] = bf16_lo(p3); x[u][7] = bf16_hi(p3);
+                hf[u][0] = hp[0];
+                hf[u][1] = hp[1];
             } else {
-                const u32x4 hv =
-                    *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(hidden) + row * H + h);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    x[u][2 * q] = bf16_lo(hv[q]);
-                    x[u][2 * q + 1] = bf16_hi(hv[q]);
-                }
+                hv[u] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(hidden) + row * H + h);
             }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (h0 + u * 64 * 8 >= H) break;
+            if constexpr (F32) {
+                // fp32 hidden values rounded to bf16 (RNE), as the projection reads them
+                hv[u][0] = pack_bf16x2(hf[u][0][0], hf[u][0][1]);
+                hv[u][1] = pack_bf16x2(hf[u][0][2], hf[u][0][3]);
+                hv[u][2] = pack_bf16x2(hf[u][1][0], hf[u][1][1]);
+                hv[u][3] = pack_bf16x2(hf[u][1][2], hf[u][1][3]);
+            }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                s += x[u][2 * q] * bf16_lo(cw[u][q]);
-                s += x[u][2 * q + 1] * bf16_hi(cw[u][q]);
+                s += bf16_lo(hv[u][q]) * bf16_lo(cw[u][q]);
+                s += bf16_hi(hv[u][q]) * bf16_hi(cw[u][q]);
             }
         }
     }
 #pragma unroll
     for (int mask = 32; mask >= 1; mask >>= 1) s += __shfl_xor(s, mask, 64);
+    return s;
+}
+__device__ __forceinline__ float slot_conf(const void* hidden, int hidden_f32, const uint16_t* conf_w,
+                                           long row, int H, int lane) {
+    const float s = hidden_f32 ? slot_conf_dot<true>(hidden, conf_w, row, H, lane)
+                               : slot_conf_dot<false>(hidden, conf_w, row, H, lane);
     return 1.0f / (1.0f + expf(-s));
 }
 
