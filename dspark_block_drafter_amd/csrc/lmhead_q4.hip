@@ -427,12 +427,12 @@ hipError_t launch_lmhead_q4(const Q4Args& a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // Tiles measured on MI355X over (FM, CTW, NS) in {1, 2, 4, 8} x {2, 4} x
-    // {2, 3, 4, 6} (prep + projection, us): Qwen3-8B shape (M = 16) 79 with
-    // <1, 2, 3> (81 <1, 2, 4>, 104 <2, 2, 4>); Gemma-4 shape (M = 24) 107 with
-    // <2, 4, 2> (114 <2, 4, 3>, 119 <2, 2, 3>); B = 8 tree (M = 128) 608 with
+    // {2, 3, 4, 6} (prep + projection, us): Qwen3-8B shape (M = 16) 71 with
+    // <1, 2, 4> (74 <1, 2, 3>, 81 <1, 2, 6>); Gemma-4 shape (M = 24) 105 with
+    // <2, 4, 2> (107 <2, 2, 3>, 109 <2, 4, 3>); B = 8 tree (M = 128) 608 with
     // <4, 2, 2> (643 <2, 4, 2>, 678 <8, 2, 2>); B = 64 (M = 1024) 4199 with
     // <4, 2, 2> (4466 <8, 2, 2>).
-    if (a.M <= 16) return run_q4<1, 2, 3>(a, stream);
+    if (a.M <= 16) return run_q4<1, 2, 4>(a, stream);
     if (a.M <= 32) return run_q4<2, 4, 2>(a, stream);
     return run_q4<4, 2, 2>(a, stream);
 }
