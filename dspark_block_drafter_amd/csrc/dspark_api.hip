@@ -621,8 +621,8 @@ int dspark_propose_q4(const void* hidden, int hidden_dtype, const void* lm_head_
     // With the bound, the 4-bit projection writes 64-column slab maxima and
     // carries the norm workgroups, as the bf16 one does; chain_init (which
     // zeroes the norm words) goes first. Its epilogue pays only where the chain
-    // prunes slabs with it (Qwen3.6-27B shape, 64 blocks of 16: 4.52 ms per
-    // step unbounded, 4.64 ms with the bound filtering top-k inserts; 16
+    // prunes slabs with it (Qwen3.8-27B shape, 64 blocks of 16: 4.52 ms per
+    // step unbounded, 4.64 ms with the bound filtering top-k inserts; 8
     // blocks, pruned: 0.889 -> 0.849 ms), so other shapes run unbounded.
     ChainExtras x;
     x.narrow_slabs = true;

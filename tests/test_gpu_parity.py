@@ -195,7 +195,14 @@ BOUND_CASES = {
     "k3_strong_markov": lambda: make_small(40, 4, 64, 20000, 32, top_k=3, w_std=0.5, seed=54),
     "k2_rank256": lambda: make_small(6, 3, 128, 9000, 256, top_k=2, w_std=0.2, seed=55),
     "k4_bias_ragged": lambda: make_small(37, 5, 320, 5003, 16, top_k=4, reachable=900, seed=56),
+    # top-1 (a running argmax: no list for the bound to filter), one block group
+    "k1_B1_r64": lambda: make_small(1, 9, 256, 50000, 64, top_k=1, conf=True, w_std=0.05, seed=57),
+    "k1_B4_bonus_reachable": lambda: make_small(4, 7, 128, 40000, 64, top_k=1, layout=BONUS_ANCHOR,
+                                                reachable=5000, conf=True, p_min=0.5, seed=58),
+    "k1_B32_rank0": lambda: make_small(32, 3, 64, 20000, 0, top_k=1, seed=60),
+    "k1_B20_V_odd": lambda: make_small(20, 4, 64, 30011, 128, top_k=1, w_std=0.5, seed=59),
 }
+
 
 
 @pytest.mark.parametrize("name", sorted(BOUND_CASES))
