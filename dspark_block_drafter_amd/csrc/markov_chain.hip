@@ -943,13 +943,16 @@ __global__ __launch_bounds__(256) void chain_step_sparse(ChainArgs a, int j) {
         const int sl = min(pb + lane, sb1 - 1);   // (sb1 > pb whenever it is called)
         const float* col = a.smax + ((long)gbase * a.n_pred + j) * nS + sl;
 #pragma unroll
-        for (int k = 0; k < 32; ++k) {
-            // rows of blocks past B are not read (their row is clamped, the value dropped)
-            const float x = col[(long)min(k, B - 1 - gbase) * a.n_pred * nS];
-            sm[k] = (exist >> k) & 1u ? x : -INFINITY;
-        }
+        for (int k = 0; k < 32; ++k)
+            // rows of blocks past B are not read (their row is clamped; the
+            // need mask drops blocks outside `exist`). Nothing here uses the
+            // values, so every load is issued before the first wait.
+            sm[k] = col[(long)min(k, B - 1 - gbase) * a.n_pred * nS];
     };
     if (sb0 < sb1) load_smax(sb0);
+    // (a compiler barrier: without it the first pass's loads are merged with
+    // the loop's and issued after the wait below, one more round trip)
+    asm volatile("" ::: "memory");
     const int prev = active ? prev_token(a, j, bme, vb == 0) : 0;
     if (lhalf == 0) s_thr[wave][lrow] = -INFINITY;
     wait_lds_reads();
