@@ -117,6 +117,12 @@ SMALL = {
     "final_wave_k1": lambda: make_small(130, 4, 64, 2000, 8, top_k=1, conf=True, p_min=0.3, seed=49),
     "final_wave_k16_bonus": lambda: make_small(70, 9, 64, 1500, 8, top_k=16, layout=BONUS_ANCHOR,
                                                seed=50),
+    # ten block groups (grid y of five pairs of groups, or ten groups), and a
+    # block of 48 prediction slots
+    "B300_ten_groups_top4": lambda: make_small(300, 3, 64, 20000, 64, top_k=4, conf=True, p_min=0.35,
+                                               seed=61),
+    "B300_ten_groups_top1": lambda: make_small(300, 3, 64, 20000, 32, top_k=1, seed=62),
+    "L48_long_block": lambda: make_small(2, 48, 64, 9000, 16, top_k=2, conf=True, p_min=0.2, seed=63),
 }
 
 
