@@ -937,13 +937,14 @@ __global__ __launch_bounds__(256) void chain_step_sparse(ChainArgs a, int j) {
     const uint32_t exist = (uint32_t)(__ballot(active) & 0xFFFFFFFFull);
     // slab maxima of the first pass (register loads issued before the wait
     // below, so they travel with the previous tokens): lane k reads slab
-    // pb + k of each of the group's blocks (rows b * n_pred + j)
-    float sm[32];
+    // pb + k of each of the group's blocks that can exist (rows b * n_pred +
+    // j; LROWS bounds them: B <= LROWS for one group)
+    float sm[LROWS];
     auto load_smax = [&](int pb) __attribute__((always_inline)) {
         const int sl = min(pb + lane, sb1 - 1);   // (sb1 > pb whenever it is called)
         const float* col = a.smax + ((long)gbase * a.n_pred + j) * nS + sl;
 #pragma unroll
-        for (int k = 0; k < 32; ++k)
+        for (int k = 0; k < LROWS; ++k)
             // rows of blocks past B are not read (their row is clamped; the
             // need mask drops blocks outside `exist`). Nothing here uses the
             // values, so every load is issued before the first wait.
@@ -1060,7 +1061,7 @@ __global__ __launch_bounds__(256) void chain_step_sparse(ChainArgs a, int j) {
         uint32_t need = 0u;
         if (pb + lane < sb1) {
 #pragma unroll
-            for (int k = 0; k < 32; ++k) need |= (sm[k] >= s_skip[wave][k] ? 1u : 0u) << k;
+            for (int k = 0; k < LROWS; ++k) need |= (sm[k] >= s_skip[wave][k] ? 1u : 0u) << k;
             need &= exist;
         }
         // compact the slabs some block needs into entries 0 .. cnt - 1
