@@ -77,6 +77,54 @@ def calibrate_copy(mib: int, reps: int) -> int:
     return 0
 
 
+def reference(d: dict, cfg, reps: int) -> dict:
+    """Ceilings from outside the library on the same shapes, for context, next
+    to the library's own projection (dspark_logits) in the same process: the
+    projection as one vendor GEMM (torch's F.linear over the prediction rows,
+    hipBLASLt; bf16 in and out, so it writes half the bytes of the library's
+    fp32 logits), and a plain device copy of 1 GiB (read and write), the rate
+    a streaming kernel can expect from HBM."""
+    import torch
+    import torch.nn.functional as F
+    i0 = 1 if cfg.layout == "bonus_anchor" else 0
+    x = d["hidden"][:, i0:, :].reshape(-1, cfg.H).contiguous()
+    w = d["lm_head"]
+    stream = torch.cuda.current_stream()
+
+    def timed(fn) -> float:
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3   # us per call
+
+    import dspark_block_drafter_amd as dsp
+    logits = torch.empty((x.shape[0], cfg.V), dtype=torch.float32, device="cuda:0")
+    def ours():
+        dsp.logits(d["hidden"], w, layout=cfg.layout, lm_head_bias=d["lm_head_bias"], out=logits,
+                   stream=stream)
+
+    # alternated, twice each, so that clock drift touches both alike
+    o1, g1, o2, g2 = timed(ours), timed(lambda: F.linear(x, w)), timed(ours), timed(lambda: F.linear(x, w))
+    ours_us, gemm_us = (o1 + o2) / 2, (g1 + g2) / 2
+    flop = 2.0 * x.shape[0] * cfg.H * cfg.V
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    copy_us = timed(lambda: dst.copy_(src))
+    return {"reference": {"workload": cfg.name, "reps": reps,
+                          "dspark_logits_fp32": {"us": ours_us, "TFLOP/s": flop / ours_us / 1e6,
+                                                 "runs_us": [o1, o2]},
+                          "hipblaslt_linear_bf16": {"us": gemm_us, "TFLOP/s": flop / gemm_us / 1e6,
+                                                    "runs_us": [g1, g2],
+                                                    "M": x.shape[0], "K": cfg.H, "N": cfg.V},
+                          "device_copy_1GiB": {"us": copy_us, "GB/s": 2.0 * src.numel() * 4 / copy_us / 1e3}}}
+
+
 def host_cpu() -> str:
     """The host's CPU model (lscpu), for the record of the CPU baseline."""
     import subprocess
@@ -136,6 +184,9 @@ def main() -> int:
     ap.add_argument("--q4", action="store_true",
                     help="run the workload with its lm_head requantized to 4-bit GGUF blocks "
                          "(dspark_q4_pack once, then dspark_propose_q4 per step)")
+    ap.add_argument("--reference", action="store_true",
+                    help="time a vendor GEMM on the projection's shape and a plain device copy "
+                         "(one JSON line; no proposal step)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -214,6 +265,9 @@ def main() -> int:
                                  stream=stream)
     else:
         d = to_device(inp)
+        if args.reference:
+            print(json.dumps(reference(d, cfg, max(args.steps, 1))), flush=True)
+            return 0
         N = cfg.V
         out = dsp.Outputs(cfg.B, cfg.L, cfg.V, cfg.top_k, cfg.layout, "cuda:0")
 
