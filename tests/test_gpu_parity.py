@@ -123,6 +123,12 @@ SMALL = {
                                                seed=61),
     "B300_ten_groups_top1": lambda: make_small(300, 3, 64, 20000, 32, top_k=1, seed=62),
     "L48_long_block": lambda: make_small(2, 48, 64, 9000, 16, top_k=2, conf=True, p_min=0.2, seed=63),
+    # a vocabulary of a million odd columns (the direct form, ~7800 workgroups
+    # and their partial lists), a thousand blocks, and a 1+1 bonus-anchor block
+    # (one predicting slot)
+    "V1M_direct_odd": lambda: make_small(2, 3, 64, 1000003, 16, top_k=2, seed=64),
+    "B1000_short": lambda: make_small(1000, 2, 64, 5000, 16, top_k=3, conf=True, p_min=0.3, seed=65),
+    "bonus_L2": lambda: make_small(3, 2, 64, 3000, 16, top_k=2, layout=BONUS_ANCHOR, seed=66),
 }
 
 
