@@ -125,6 +125,45 @@ def reference(d: dict, cfg, reps: int) -> dict:
                           "device_copy_1GiB": {"us": copy_us, "GB/s": 2.0 * src.numel() * 4 / copy_us / 1e3}}}
 
 
+def graph_timing(d: dict, cfg, steps: int) -> dict:
+    """dspark_propose_noalloc eagerly, and the same call captured once in a
+    HIP graph and replayed (the launches of a step issued as one graph),
+    alternated twice each in one process: the cost of the step's launches."""
+    import torch
+    import dspark_block_drafter_amd as dsp
+    out = dsp.Outputs(cfg.B, cfg.L, cfg.V, cfg.top_k, cfg.layout, "cuda:0")
+
+    def call():
+        dsp.propose_noalloc(d["hidden"], d["lm_head"], d["markov_w1"], d["markov_w2"], d["anchors"],
+                            layout=cfg.layout, top_k=cfg.top_k, p_min=cfg.p_min,
+                            lm_head_bias=d["lm_head_bias"], conf_w=d["conf_w"], out=out)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def timed(fn) -> float:
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps * 1e3   # us per step
+
+    e1_, g1, e2_, g2 = timed(call), timed(g.replay), timed(call), timed(g.replay)
+    return {"graph": {"workload": cfg.name, "steps": steps,
+                      "eager_noalloc_us": (e1_ + e2_) / 2, "graph_replay_us": (g1 + g2) / 2,
+                      "runs_us": {"eager": [e1_, e2_], "replay": [g1, g2]}}}
+
+
 def host_cpu() -> str:
     """The host's CPU model (lscpu), for the record of the CPU baseline."""
     import subprocess
@@ -187,6 +226,9 @@ def main() -> int:
     ap.add_argument("--reference", action="store_true",
                     help="time a vendor GEMM on the projection's shape and a plain device copy "
                          "(one JSON line; no proposal step)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time dspark_propose_noalloc eagerly and as a replayed HIP graph "
+                         "(one JSON line; no proposal record)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -267,6 +309,9 @@ def main() -> int:
         d = to_device(inp)
         if args.reference:
             print(json.dumps(reference(d, cfg, max(args.steps, 1))), flush=True)
+            return 0
+        if args.graph:
+            print(json.dumps(graph_timing(d, cfg, max(args.steps, 1))), flush=True)
             return 0
         N = cfg.V
         out = dsp.Outputs(cfg.B, cfg.L, cfg.V, cfg.top_k, cfg.layout, "cuda:0")
