@@ -1316,11 +1316,12 @@ __device__ __forceinline__ int final_token(const FinalArgs& a, u64 key) {
 // same results:
 //  * finalize_group: one workgroup per (slot, block), eight keys per thread
 //    in flight, then a wave merge and an LDS merge;
-//  * finalize_wave: one wave per (block, slot), four per workgroup, 16 keys
-//    per lane in flight. With many pairs a workgroup per pair costs more in
-//    launch and dispatch than in merging (at B = 64, 1024 pairs: 31 -> 22 us);
-//    with few (B = 8: 128 pairs) it spreads the merge over more CUs (12
-//    against 14.5 us).
+//  * finalize_wave: two waves per (block, slot), two pairs per workgroup:
+//    the candidates (16 keys per lane in flight, then a wave merge) on one,
+//    the confidence on the other. With many pairs a workgroup per pair costs
+//    more in launch and dispatch than in merging (at B = 64, 1024 pairs: 31
+//    us, against 22 with one wave per pair and 14 with two); with few (B = 8:
+//    128 pairs) it spreads the merge over more CUs (12 against 14.5 us).
 
 template <int KL>
 __global__ __launch_bounds__(256) void finalize_group(FinalArgs a) {
@@ -1408,12 +1409,26 @@ __global__ __launch_bounds__(256) void finalize_group(FinalArgs a) {
 
 template <int KL>
 __global__ __launch_bounds__(256) void finalize_wave(FinalArgs a) {
-    // one wave per (block, slot); pair = b * n_pred + j is the output row
+    // two waves per (block, slot), pair = b * n_pred + j the output row: the
+    // candidates on the even wave and the confidence on the odd one, side by
+    // side (in one wave the two ran one after the other: 6.7 + 10.6 us)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int B = a.B, n = a.n_pred, k = a.top_k;
-    const long o = (long)blockIdx.x * kWaves + wave;
+    const long o = (long)blockIdx.x * (kWaves / 2) + (wave >> 1);
     if (o >= (long)B * n) return;
     const int b = (int)(o / n), j = (int)(o - (long)b * n);
+    if (wave & 1) {
+        // Confidence head (with the adaptive gate it was computed before the chain).
+        if (!a.gated) {
+            float c = 1.0f;
+            if (a.conf_w) {
+                c = slot_conf(a.hidden, a.hidden_f32, a.conf_w, (long)b * a.L + a.i_first + j, a.H, lane);
+                if (lane == 0 && c < a.p_min) atomicMin(a.lengths + b, j);
+            }
+            if (lane == 0 && a.conf) a.conf[o] = c;
+        }
+        return;
+    }
 
     // Adaptive gate: a slot past its block's cut was not drafted, and a block
     // keeps only its own number of candidates.
@@ -1428,24 +1443,13 @@ __global__ __launch_bounds__(256) void finalize_wave(FinalArgs a) {
     }
     const u64 win = winner_key(a.winners, a.wstride, j, b);
 
-    // The first keys of the partial lists are loaded before the confidence,
-    // so that both sets of loads are in flight together.
+    // the first keys of the partial lists, 16 per lane in flight
     constexpr int U = 16;
     const u64* p = a.partials + ((long)j * B + b) * a.nwg * k;
     const int cnt = k > 1 ? a.nwg * k : 0;
     u64 kk[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) kk[u] = lane + u * kWave < cnt ? p[lane + u * kWave] : 0ull;
-
-    // Confidence head (with the adaptive gate it was computed before the chain).
-    if (!a.gated) {
-        float c = 1.0f;
-        if (a.conf_w) {
-            c = slot_conf(a.hidden, a.hidden_f32, a.conf_w, (long)b * a.L + a.i_first + j, a.H, lane);
-            if (lane == 0 && c < a.p_min) atomicMin(a.lengths + b, j);
-        }
-        if (lane == 0 && a.conf) a.conf[o] = c;
-    }
 
     if (k == 1) {
         if (lane == 0) {
@@ -1723,7 +1727,7 @@ hipError_t launch_finalize(const FinalArgs& a, hipStream_t stream) {
     else if (a.top_k <= 8) hipLaunchKernelGGL(KERNEL<8>, GRID, block, 0, stream, a);         \
     else hipLaunchKernelGGL(KERNEL<16>, GRID, block, 0, stream, a);
     if (pairs >= kFinalWavePairs) {
-        DSPARK_FINAL(finalize_wave, dim3((unsigned)((pairs + kWaves - 1) / kWaves)))
+        DSPARK_FINAL(finalize_wave, dim3((unsigned)((pairs + kWaves / 2 - 1) / (kWaves / 2))))
     } else {
         DSPARK_FINAL(finalize_group, dim3(a.n_pred, a.B))
     }
