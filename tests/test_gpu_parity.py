@@ -117,6 +117,9 @@ SMALL = {
     "final_wave_k1": lambda: make_small(130, 4, 64, 2000, 8, top_k=1, conf=True, p_min=0.3, seed=49),
     "final_wave_k16_bonus": lambda: make_small(70, 9, 64, 1500, 8, top_k=16, layout=BONUS_ANCHOR,
                                                seed=50),
+    # an odd number of (block, slot) pairs: the last workgroup holds one pair
+    "final_wave_odd_pairs": lambda: make_small(103, 5, 64, 2500, 16, top_k=4, conf=True, p_min=0.4,
+                                               seed=101),
     # ten block groups (grid y of five pairs of groups, or ten groups), and a
     # block of 48 prediction slots
     "B300_ten_groups_top4": lambda: make_small(300, 3, 64, 20000, 64, top_k=4, conf=True, p_min=0.35,
@@ -374,6 +377,8 @@ ADAPTIVE = {
                                        seed=63),
     "adaptive_B72_final_wave": lambda: make_small(72, 8, 64, 2048, 16, top_k=4, conf=True,
                                                   conf_trend=True, seed=64),
+    "adaptive_odd_pairs_final_wave": lambda: make_small(75, 7, 64, 2048, 16, top_k=4, conf=True,
+                                                        conf_trend=True, seed=102),
 }
 
 
