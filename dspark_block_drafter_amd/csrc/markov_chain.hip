@@ -33,7 +33,7 @@ namespace dspark {
 namespace {
 
 constexpr int kWaves = 4;
-// finalize runs one wave per (block, slot) from this many pairs on, one
+// finalize runs two waves per (block, slot) from this many pairs on, one
 // workgroup per pair below it.
 constexpr long kFinalWavePairs = 512;
 static_assert(kChainTileV == kWaves * 32, "one 32-column block per wave");
