@@ -40,7 +40,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 GEMM_TRAFFIC = {
     "workload": "qwen38_27b_throughput",
     "source_sha256": "6aaf425b8a82f80e734bb6da1d0d745c2844622dc6c9f2588090d0a7e190595b",
-    "bytes": 5594072754,
+    "bytes": 5759954386,
 }
 
 
