@@ -54,6 +54,14 @@ SMALL = {
     "single_slot": lambda: make_small(1, 1, 32, 33, 8, top_k=1, seed=7),
     "mid_gemm_M33": lambda: make_small(11, 3, 1032, 4097, 32, top_k=2, seed=8),
     "rank256": lambda: make_small(6, 4, 128, 1536, 256, top_k=3, seed=9, w_std=0.2),
+    # ranks above 128: the three-stage ring over two block groups (top-4 and
+    # top-1), the same ring at top-1 with the rank padded from 200, and the
+    # direct kernel (V % 4 != 0) with one and two block groups
+    "B40_r256_top4": lambda: make_small(40, 3, 128, 4096, 256, top_k=4, w_std=0.2, seed=111),
+    "B40_r256_top1": lambda: make_small(40, 3, 128, 4096, 256, top_k=1, w_std=0.2, seed=112),
+    "r200_top1": lambda: make_small(6, 3, 128, 3000, 200, top_k=1, w_std=0.2, seed=113),
+    "r256_V_odd": lambda: make_small(5, 3, 128, 3001, 256, top_k=2, w_std=0.2, seed=114),
+    "B40_r192_V_odd": lambda: make_small(40, 3, 64, 2003, 192, top_k=3, w_std=0.2, seed=115),
     "dma_mid_M63": lambda: make_small(9, 7, 160, 3001, 16, top_k=2, conf=True, p_min=0.4, seed=18),
     # 32 < M <= 128 with H % 64 == 0 and too few 256-row tiles for the CUs:
     # the 128-row tiles with 64-value stage rows, ragged M and N
