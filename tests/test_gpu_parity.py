@@ -320,6 +320,11 @@ D2T_SMALL = {
     "d2t_top1_r64": lambda: make_small(3, 9, 64, 5000, 64, top_k=1, reachable=1031, seed=42),
     "d2t_ragged_D": lambda: make_small(37, 6, 128, 2000, 8, top_k=2, reachable=333, seed=43),
     "d2t_topk_equals_D": lambda: make_small(2, 4, 32, 700, 8, top_k=5, reachable=5, seed=44),
+    # fp32 hidden states (the register-staged projection over D rows), and
+    # top-1 over two block groups
+    "d2t_f32_hidden": lambda: make_small(9, 5, 96, 3000, 16, top_k=3, hidden_f32=True, reachable=512,
+                                         conf=True, p_min=0.4, seed=116),
+    "d2t_B40_top1": lambda: make_small(40, 4, 64, 3000, 16, top_k=1, reachable=700, seed=117),
 }
 
 
