@@ -392,6 +392,14 @@ ADAPTIVE = {
                                                   conf_trend=True, seed=64),
     "adaptive_odd_pairs_final_wave": lambda: make_small(75, 7, 64, 2048, 16, top_k=4, conf=True,
                                                         conf_trend=True, seed=102),
+    # top-1 (the per-wave form) with one and two block groups, and a rank
+    # above 128 (the three-stage ring) over two block groups
+    "adaptive_top1": lambda: make_small(6, 8, 96, 3000, 16, top_k=1, conf=True, conf_trend=True,
+                                        seed=118),
+    "adaptive_B40_top1": lambda: make_small(40, 6, 64, 3000, 16, top_k=1, conf=True,
+                                            conf_trend=True, seed=119),
+    "adaptive_B36_r256": lambda: make_small(36, 5, 64, 2048, 256, top_k=3, conf=True,
+                                            conf_trend=True, w_std=0.2, seed=120),
 }
 
 
