@@ -114,6 +114,10 @@ PROPOSE = {
                                           seed=81), "round"),
     "B40_k16_f32": (lambda: make_small(40, 3, 128, 1111, 32, top_k=16, hidden_f32=True, seed=82),
                     "random"),
+    # top-1 over two block groups; a rank above 128 (the three-stage ring)
+    "B40_top1_conf": (lambda: make_small(40, 4, 128, 3000, 16, top_k=1, conf=True, p_min=0.4,
+                                         seed=121), "random"),
+    "B6_r256": (lambda: make_small(6, 3, 128, 2048, 256, top_k=3, w_std=0.2, seed=122), "round"),
 }
 
 
